@@ -1,0 +1,92 @@
+// Shared device helpers for the SPA-Cache kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spa {
+
+typedef uint16_t bf16_t;  // raw bfloat16 storage (upper half of an IEEE binary32)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bfloat16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// Elements per 16-byte vector.
+template <typename T> struct Vec { static constexpr int kN = 16 / sizeof(T); };
+
+// Unpack a 16-byte vector of T into floats.
+__device__ __forceinline__ void unpack16(const u32x4 &v, float *out, const bf16_t *) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(v[j] << 16);
+    out[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack16(const u32x4 &v, float *out, const float *) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(v[j]);
+}
+__device__ __forceinline__ u32x4 pack16(const float *in, const bf16_t *) {
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(in[2 * j], in[2 * j + 1]);
+  return v;
+}
+__device__ __forceinline__ u32x4 pack16(const float *in, const float *) {
+  u32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = __float_as_uint(in[j]);
+  return v;
+}
+
+// 16x16 MFMA tiles. bf16: K = 32 per instruction, 8 values per lane (k = 8*(lane/16) + 0..7).
+// fp32: K = 4 per instruction, 1 value per lane (k = lane/16). Output: lane holds column lane%16,
+// rows 4*(lane/16) + 0..3. The k order inside an instruction only has to agree between A and B.
+__device__ __forceinline__ floatx4 mfma16(const u32x4 &a, const u32x4 &b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+}  // namespace spa

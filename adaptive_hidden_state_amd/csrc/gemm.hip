@@ -1,0 +1,341 @@
+// MFMA GEMM C = A W^T with the fused epilogues of the SPA-Cache sparse update
+// ([PN] 整体框架 phases 2 and 3: Q/K/V of the update set with the K/V cache scatter, W_o with the
+// residual, the SwiGLU gate/up product, and W_down with the residual scattered into H^c).
+//
+// A (M x K) and W (rows x K) are both K-contiguous, which is the operand order the 16x16 MFMA wants:
+// every lane reads 16 contiguous bytes of a row for each k-step. Tiles are staged through LDS in
+// 128-byte K slabs (64 bf16 / 32 fp32), double-buffered, with a 16-byte row pad so that the 16 rows a
+// quarter-wave reads land on distinct LDS banks. Workgroups of one XCD get a contiguous range of
+// tiles, M fastest, so tiles that share a weight panel run together behind the same L2.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace spa {
+
+// Output column n of the gate/up GEMM -> row of W = [gate; up] (2F x d). Columns come in groups of
+// 32: the first 16 are gate rows 16q..16q+15, the next 16 the up rows with the same j, so that one
+// lane of an MFMA tile holds gate and up of the same hidden unit.
+__device__ __forceinline__ int swiglu_wrow(int n, int f) {
+  const int q = n >> 5, w = n & 31;
+  return (w < 16) ? (q * 16 + w) : (f + q * 16 + w - 16);
+}
+
+__device__ __forceinline__ int map_token(const EpiArgs &ea, int m, int &b) {
+  b = m / ea.k_per_seq;
+  return ea.idx ? ea.idx[m] : (m - b * ea.k_per_seq);
+}
+
+template <typename T, int KIND>
+__device__ __forceinline__ void epi_store(const EpiArgs &ea, int m, int n, float v) {
+  if constexpr (KIND == kEpiQKV) {
+    if (n < ea.dq) {
+      ((T *)ea.out)[(size_t)m * ea.dq + n] = from_f32<T>(v);
+      return;
+    }
+    int b;
+    const int i = map_token(ea, m, b);
+    if ((unsigned)i >= (unsigned)ea.n_tok) return;
+    int nn = n - ea.dq;
+    T *dst = (T *)ea.out2;
+    if (nn >= ea.dkv) {
+      nn -= ea.dkv;
+      dst = (T *)ea.out3;
+    }
+    const int g = nn / ea.hd, e = nn - g * ea.hd;
+    dst[(((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e] = from_f32<T>(v);
+  } else if constexpr (KIND == kEpiResid) {
+    int b;
+    int i = map_token(ea, m, b);
+    i = min(max(i, 0), ea.n_tok - 1);
+    const float r = to_f32<T>(((const T *)ea.src)[((size_t)b * ea.n_tok + i) * ea.ld_src + n]);
+    ((T *)ea.out)[(size_t)m * ea.ldo + n] = from_f32<T>(r + v);
+  } else if constexpr (KIND == kEpiResidScatter) {
+    int b;
+    const int i = map_token(ea, m, b);
+    if ((unsigned)i >= (unsigned)ea.n_tok) return;
+    const float r = to_f32<T>(((const T *)ea.src)[(size_t)m * ea.ld_src + n]);
+    ((T *)ea.out)[((size_t)b * ea.n_tok + i) * ea.ldo + n] = from_f32<T>(r + v);
+  } else if constexpr (KIND == kEpiPartial) {
+    ((float *)ea.out)[(size_t)m * ea.ldo + n] = v;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_swiglu(const EpiArgs &ea, int m, int j, float g, float u) {
+  const float s = g / (1.0f + __expf(-g));
+  ((T *)ea.out)[(size_t)m * ea.f + j] = from_f32<T>(s * u);
+}
+
+template <int KIND>
+__device__ __forceinline__ int weight_row(int n, const EpiArgs &ea) {
+  if constexpr (KIND == kEpiSwiGLU) return swiglu_wrow(n, ea.f);
+  return n;
+}
+
+template <bool BF16> struct Frag;
+template <> struct Frag<true> { typedef u32x4 type; };
+template <> struct Frag<false> { typedef float type; };
+
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int KIND>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
+    const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, int M, int N, int K, int tiles_m,
+    int tiles_n, int k_split, float *__restrict__ part, EpiArgs ea) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int BK = 128 / sizeof(T);
+  constexpr int ROWB = 144;
+  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  constexpr int A_PER = BM * 8 / NT, B_PER = BN * 8 / NT;
+  constexpr bool IS_BF16 = sizeof(T) == 2;
+  constexpr int KSTEPS = IS_BF16 ? 2 : 8;
+  constexpr int KSTEP_B = IS_BF16 ? 64 : 16;
+  constexpr int LANE_B = IS_BF16 ? 16 : 4;
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles are made of 16x16 blocks");
+  static_assert(KIND != kEpiSwiGLU || (WTN % 32 == 0), "gate/up pairs must stay inside a wave");
+  typedef typename Frag<IS_BF16>::type FragT;
+
+  __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m;
+  const int rest = bid / tiles_m;
+  const int tn = rest % tiles_n;
+  const int split = rest / tiles_n;
+  const int k0 = split * k_split;
+  const int k1 = min(K, k0 + k_split);
+  const int nk = k1 > k0 ? (k1 - k0 + BK - 1) / BK : 0;
+
+  const char *a_src[A_PER];
+  const char *b_src[B_PER];
+  int a_dst[A_PER], b_dst[B_PER], a_k[A_PER], b_k[B_PER];
+#pragma unroll
+  for (int j = 0; j < A_PER; ++j) {
+    const int c = tid + j * NT, row = c >> 3, col = c & 7;
+    const int gr = min(tm * BM + row, M - 1);
+    a_src[j] = reinterpret_cast<const char *>(A + (size_t)gr * lda + k0) + col * 16;
+    a_dst[j] = row * ROWB + col * 16;
+    a_k[j] = k0 + col * VEC;
+  }
+#pragma unroll
+  for (int j = 0; j < B_PER; ++j) {
+    const int c = tid + j * NT, row = c >> 3, col = c & 7;
+    const int gr = weight_row<KIND>(min(tn * BN + row, N - 1), ea);
+    b_src[j] = reinterpret_cast<const char *>(W + (size_t)gr * ldw + k0) + col * 16;
+    b_dst[j] = BM * ROWB + row * ROWB + col * 16;
+    b_k[j] = k0 + col * VEC;
+  }
+
+  u32x4 ra[A_PER], rb[B_PER];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto gload = [&](int kt) {
+    const int kb = kt * BK;
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) ra[j] = (a_k[j] + kb < k1) ? ld16(a_src[j] + kb * sizeof(T)) : zero;
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) rb[j] = (b_k[j] + kb < k1) ? ld16(b_src[j] + kb * sizeof(T)) : zero;
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) st16(&lds[buf][a_dst[j]], ra[j]);
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j) st16(&lds[buf][b_dst[j]], rb[j]);
+  };
+
+  floatx4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  const int frag_off = (lane & 15) * ROWB + (lane >> 4) * LANE_B;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const char *As = &lds[cur][(wm * WTM) * ROWB + frag_off];
+    const char *Bs = &lds[cur][BM * ROWB + (wn * WTN) * ROWB + frag_off];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      FragT af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const FragT *>(As + i * 16 * ROWB + ks * KSTEP_B);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const FragT *>(Bs + j * 16 * ROWB + ks * KSTEP_B);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  const int row0 = tm * BM + wm * WTM + (lane >> 4) * 4;
+  const int col0 = tn * BN + wn * WTN + (lane & 15);
+  if (part != nullptr) {
+    float *P = part + (size_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = row0 + i * 16 + r, n = col0 + j * 16;
+          if (m < M && n < N) P[(size_t)m * N + n] = acc[i][j][r];
+        }
+    return;
+  }
+  if constexpr (KIND == kEpiSwiGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; j += 2)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = row0 + i * 16 + r, n = col0 + j * 16;
+          if (m < M && n < N) epi_swiglu<T>(ea, m, (n >> 5) * 16 + (n & 31), acc[i][j][r], acc[i][j + 1][r]);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = row0 + i * 16 + r, n = col0 + j * 16;
+          if (m < M && n < N) epi_store<T, KIND>(ea, m, n, acc[i][j][r]);
+        }
+  }
+}
+
+// Sum of the split-K partials in split order (deterministic), then the epilogue.
+template <typename T, int KIND>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits, int M,
+                                                            int N, EpiArgs ea) {
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t plane = (size_t)M * N;
+  if constexpr (KIND == kEpiSwiGLU) {
+    const int f = ea.f;
+    if (t >= (size_t)M * f) return;
+    const int m = (int)(t / f), j = (int)(t - (size_t)m * f);
+    const int ng = (j >> 4) * 32 + (j & 15);
+    float g = 0.f, u = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      g += part[s * plane + (size_t)m * N + ng];
+      u += part[s * plane + (size_t)m * N + ng + 16];
+    }
+    epi_swiglu<T>(ea, m, j, g, u);
+  } else {
+    if (t >= plane) return;
+    const int m = (int)(t / N), n = (int)(t - (size_t)m * N);
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += part[s * plane + t];
+    epi_store<T, KIND>(ea, m, n, v);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// host side: tile plans and dispatch
+// ---------------------------------------------------------------------------------------------
+namespace {
+constexpr int kTargetWGs = 256;  // one workgroup per CU of an MI355X
+
+struct TileCfg {
+  int bm, bn;
+};
+// cfg 0: fp32, 64x64 (2x2 waves); cfg 1: bf16 128x128 (2x2 waves of 64x64); cfg 2: bf16 64x128 (1x4)
+constexpr TileCfg kTiles[3] = {{64, 64}, {128, 128}, {64, 128}};
+}  // namespace
+
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
+  GemmPlan p{};
+  p.cfg = dtype == kF32 ? 0 : (M >= 128 ? 1 : 2);
+  p.bm = kTiles[p.cfg].bm;
+  p.bn = kTiles[p.cfg].bn;
+  p.tiles_m = (M + p.bm - 1) / p.bm;
+  p.tiles_n = (N + p.bn - 1) / p.bn;
+  const int bk = dtype == kF32 ? 32 : 64;
+  const int tiles = p.tiles_m * p.tiles_n;
+  int splits = 1;
+  if (kind == kEpiPartial || tiles < kTargetWGs / 2) {
+    const int max_splits = K / (bk * 4) > 1 ? K / (bk * 4) : 1;
+    splits = (kTargetWGs + tiles - 1) / tiles;
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+  }
+  int ks = (K + splits - 1) / splits;
+  ks = (ks + bk - 1) / bk * bk;
+  p.k_split = ks;
+  p.splits = (K + ks - 1) / ks;
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+size_t gemm_partial_bytes(const GemmPlan &p, int M, int N) {
+  return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+template <typename T, int BM, int BN, int WMv, int WNv, int KIND>
+static hipError_t run_gemm(const GemmPlan &p, const void *A, int lda, const void *W, int ldw, int M, int N,
+                           int K, float *part, const EpiArgs &ea, hipStream_t s) {
+  const bool use_part = (KIND == kEpiPartial) || p.splits > 1;
+  const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
+  EpiArgs e = ea;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WMv, WNv, KIND>), dim3(grid), dim3(64 * WMv * WNv), 0, s,
+                     (const T *)A, lda, (const T *)W, ldw, M, N, K, p.tiles_m, p.tiles_n, p.k_split,
+                     use_part ? part : nullptr, e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || KIND == kEpiPartial || p.splits == 1) return err;
+  const size_t work = KIND == kEpiSwiGLU ? (size_t)M * ea.f : (size_t)M * N;
+  const unsigned rgrid = (unsigned)((work + 255) / 256);
+  hipLaunchKernelGGL((splitk_reduce_kernel<T, KIND>), dim3(rgrid), dim3(256), 0, s, part, p.splits, M, N, e);
+  return hipGetLastError();
+}
+
+template <typename T, int KIND>
+static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void *W, int ldw, int M, int N, int K,
+                          float *part, const EpiArgs &ea, hipStream_t s) {
+  switch (p.cfg) {
+    case 0: return run_gemm<T, 64, 64, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    case 1: return run_gemm<T, 128, 128, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    default: return run_gemm<T, 64, 128, 1, 4, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+  }
+}
+
+template <typename T>
+static hipError_t run_kind(int kind, const GemmPlan &p, const void *A, int lda, const void *W, int ldw, int M,
+                           int N, int K, float *part, const EpiArgs &ea, hipStream_t s) {
+  switch (kind) {
+    case kEpiPartial: return run_cfg<T, kEpiPartial>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    case kEpiQKV: return run_cfg<T, kEpiQKV>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    case kEpiResid: return run_cfg<T, kEpiResid>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    case kEpiSwiGLU: return run_cfg<T, kEpiSwiGLU>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    case kEpiResidScatter: return run_cfg<T, kEpiResidScatter>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W, int ldw,
+                       int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (dtype == kF32) {
+    // fp32 uses the single 64x64 configuration
+    GemmPlan p = plan;
+    return run_kind<float>(kind, p, A, lda, W, ldw, M, N, K, part, ea, s);
+  }
+  return run_kind<bf16_t>(kind, plan, A, lda, W, ldw, M, N, K, part, ea, s);
+}
+
+}  // namespace spa

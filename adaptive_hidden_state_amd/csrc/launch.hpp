@@ -1,0 +1,68 @@
+// Internal launchers of the SPA-Cache kernels. Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace spa {
+
+enum DTypeId { kF32 = 0, kBF16 = 1 };
+
+// Epilogue of a GEMM C = A W^T (A: M x K, W: rows x K, both K-contiguous).
+enum EpiKind {
+  kEpiPartial = 0,       // fp32 partial sums [split][M][N] (split-K, and the proxy projection)
+  kEpiQKV = 1,           // columns [0,dq) -> Q (M x dq); [dq,dq+dkv) -> K^c[row]; rest -> V^c[row]
+  kEpiResid = 2,         // out[m][n] = src[row(m)][n] + acc     (W_o with the residual of x)
+  kEpiSwiGLU = 3,        // W = [gate; up] (2F rows): z[m][j] = silu(gate) * up
+  kEpiResidScatter = 4,  // out[row(m)][n] = src[m][n] + acc     (W_down + residual into H^c)
+};
+
+// Row m of a GEMM over update sets: sequence b = m / k_per_seq, token i = idx ? idx[m] : m % k_per_seq,
+// and the token's row in a B x N x ... tensor is b * n_tok + i. Out-of-range i is skipped on writes.
+struct EpiArgs {
+  void *out;
+  void *out2;
+  void *out3;
+  const void *src;
+  const int32_t *idx;
+  int k_per_seq;
+  int n_tok;
+  int dq, dkv, hkv, hd;
+  int ld_src;
+  int ldo;
+  int f;
+};
+
+struct GemmPlan {
+  int cfg;       // tile configuration id
+  int bm, bn;
+  int tiles_m, tiles_n;
+  int splits;    // > 1: fp32 partials + a reduce kernel that applies the epilogue
+  int k_split;   // K elements per split (multiple of the K slab)
+};
+
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
+size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
+
+// part: workspace for fp32 partials (gemm_partial_bytes), required when plan.splits > 1 or kind is
+// kEpiPartial (then the partials are the result).
+hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W,
+                       int ldw, int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s);
+
+// Phase 1 pieces.
+hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,
+                               float *pc_write, float *p_out, float *scores, hipStream_t s);
+hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s);
+hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *idx, int batch, int n,
+                                int k, int r, hipStream_t s);
+
+// RMSNorm of rows (optionally gathered through an update set) into a dense M x d buffer.
+hipError_t launch_rmsnorm(int dtype, const void *src, const int32_t *idx, int k_per_seq, int n_tok,
+                          int rows, int d, const void *g, float eps, void *dst, hipStream_t s);
+
+// Sparse-query attention: q (B*m_per_seq x hq*hd) against K^c/V^c (B x hkv x n_tok x hd).
+hipError_t launch_attention(int dtype, const void *q, const void *kc, const void *vc, void *o, int batch,
+                            int m_per_seq, int n_tok, int hq, int hkv, int hd, hipStream_t s);
+
+}  // namespace spa

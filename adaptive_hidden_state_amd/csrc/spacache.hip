@@ -1,0 +1,385 @@
+// C ABI of libspacache: argument validation, workspace layout and the launch sequence of the
+// SPA-Cache layer step ([PN] 整体框架, Algorithm 1's three phases). Every check runs on the host
+// before the first launch, so invalid calls fail without touching the GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.hpp"
+#include "spacache.h"
+
+using namespace spa;
+
+namespace {
+
+struct Dims {
+  int B, N, d, hq, hkv, hd, F, r, dq, dkv, e, dtype;
+  float eps;
+};
+
+int check_shape(const spa_shape *s, Dims *o) {
+  if (s == nullptr) return SPA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->n_tokens < 1 || s->d_model < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 ||
+      s->head_dim < 1 || s->d_ffn < 1 || s->rank < 1)
+    return SPA_ERR_INVALID_ARG;
+  if (!(s->norm_eps >= 0.0f) || !isfinite(s->norm_eps)) return SPA_ERR_INVALID_ARG;
+  if (s->dtype != SPA_F32 && s->dtype != SPA_BF16) return SPA_ERR_UNSUPPORTED;
+  if (s->n_tokens > 16384) return SPA_ERR_UNSUPPORTED;
+  if (s->d_model % 64 != 0 || s->d_ffn % 16 != 0) return SPA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return SPA_ERR_UNSUPPORTED;
+  if (s->n_q_heads % s->n_kv_heads != 0) return SPA_ERR_UNSUPPORTED;
+  const long long dkv = (long long)s->n_kv_heads * s->head_dim;
+  const long long dq = (long long)s->n_q_heads * s->head_dim;
+  if (s->rank % 16 != 0 || s->rank > 1024 || s->rank > s->d_model || s->rank > dkv) return SPA_ERR_UNSUPPORTED;
+  // every index computed in 32 bits stays below 2^31
+  const long long rows = (long long)s->batch * s->n_tokens;
+  long long widest = 2LL * s->d_ffn;
+  if (dq + 2 * dkv > widest) widest = dq + 2 * dkv;
+  if (s->d_model > widest) widest = s->d_model;
+  if (rows * widest >= (1LL << 31) || dq > (1 << 20) || dkv > (1 << 20)) return SPA_ERR_UNSUPPORTED;
+  o->B = s->batch;
+  o->N = s->n_tokens;
+  o->d = s->d_model;
+  o->hq = s->n_q_heads;
+  o->hkv = s->n_kv_heads;
+  o->hd = s->head_dim;
+  o->F = s->d_ffn;
+  o->r = s->rank;
+  o->dq = (int)dq;
+  o->dkv = (int)dkv;
+  o->dtype = s->dtype;
+  o->e = s->dtype == SPA_BF16 ? 2 : 4;
+  o->eps = s->norm_eps;
+  return SPA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Workspace regions. Offsets are multiples of 256 bytes.
+struct Layout {
+  GemmPlan proxy;
+  size_t ppart, pbuf, scores, a1, q, o, y, b1, z, gpart, total;
+};
+
+Layout make_layout(const Dims &D, int k_max) {
+  Layout L{};
+  const size_t rows = (size_t)D.B * D.N;
+  const size_t m = (size_t)D.B * (size_t)k_max;
+  L.proxy = plan_gemm(D.dtype, (int)rows, D.r, D.d, kEpiPartial);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  L.ppart = take(gemm_partial_bytes(L.proxy, (int)rows, D.r));
+  L.pbuf = take(rows * D.r * 4);
+  L.scores = take(rows * 4);
+  L.a1 = take(m * D.d * D.e);
+  L.q = take(m * D.dq * D.e);
+  L.o = take(m * D.dq * D.e);
+  L.y = take(m * D.d * D.e);
+  L.b1 = take(m * D.d * D.e);
+  L.z = take(m * D.F * D.e);
+  // Split-K partials are only used when a GEMM has fewer than 128 tiles; then
+  // splits * M * N < (256 + tiles) * BM * BN <= 384 * 128 * 128.
+  size_t gp = 0;
+  const int Ms[1] = {(int)m};
+  for (int mm : Ms) {
+    if (mm <= 0) continue;
+    const int shapes[4][3] = {{D.dq + 2 * D.dkv, D.d, kEpiQKV}, {D.d, D.dq, kEpiResid},
+                              {2 * D.F, D.d, kEpiSwiGLU}, {D.d, D.F, kEpiResidScatter}};
+    for (auto &sh : shapes) {
+      const GemmPlan p = plan_gemm(D.dtype, mm, sh[0], sh[1], sh[2]);
+      if (p.splits > 1) {
+        const size_t b = gemm_partial_bytes(p, mm, sh[0]);
+        if (b > gp) gp = b;
+      }
+    }
+  }
+  const size_t bound = (D.dtype == SPA_BF16 ? 384ull * 128 * 128 : 384ull * 64 * 64) * 4;
+  if (m > 0 && gp < bound) gp = bound;
+  L.gpart = take(gp);
+  L.total = off;
+  return L;
+}
+
+char *at(void *ws, size_t off) { return (char *)ws + off; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SPA_OK : SPA_ERR_HIP; }
+
+#define SPA_TRY(expr)                              \
+  do {                                             \
+    const hipError_t _e = (expr);                  \
+    if (_e != hipSuccess) return SPA_ERR_HIP;      \
+  } while (0)
+
+int check_weights(const spa_layer_weights *w) {
+  if (w == nullptr) return SPA_ERR_INVALID_ARG;
+  const void *p[7] = {w->w_r, w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->g_attn, w->g_ffn};
+  for (const void *x : p) {
+    if (x == nullptr) return SPA_ERR_INVALID_ARG;
+    if (!aligned16(x)) return SPA_ERR_ALIGN;
+  }
+  return SPA_OK;
+}
+
+int check_cache(const spa_layer_cache *c, const Dims &D, const void *h_in) {
+  if (c == nullptr || c->k_cache == nullptr || c->v_cache == nullptr || c->h_cache == nullptr ||
+      c->p_cache == nullptr || h_in == nullptr)
+    return SPA_ERR_INVALID_ARG;
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || !aligned16(c->h_cache) || !aligned16(c->p_cache) ||
+      !aligned16(h_in))
+    return SPA_ERR_ALIGN;
+  const size_t xb = (size_t)D.B * D.N * D.d * D.e;
+  const size_t kvb = (size_t)D.B * D.hkv * D.N * D.hd * D.e;
+  const size_t pb = (size_t)D.B * D.N * D.r * 4;
+  if (overlap(h_in, xb, c->h_cache, xb) || overlap(h_in, xb, c->k_cache, kvb) ||
+      overlap(h_in, xb, c->v_cache, kvb) || overlap(h_in, xb, c->p_cache, pb))
+    return SPA_ERR_ALIAS;
+  if (overlap(c->k_cache, kvb, c->v_cache, kvb) || overlap(c->h_cache, xb, c->k_cache, kvb) ||
+      overlap(c->h_cache, xb, c->v_cache, kvb) || overlap(c->p_cache, pb, c->h_cache, xb) ||
+      overlap(c->p_cache, pb, c->k_cache, kvb) || overlap(c->p_cache, pb, c->v_cache, kvb))
+    return SPA_ERR_ALIAS;
+  return SPA_OK;
+}
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+  if (need > ws_bytes) return SPA_ERR_WORKSPACE;
+  if (need > 0 && ws == nullptr) return SPA_ERR_WORKSPACE;
+  if (ws != nullptr && !aligned16(ws)) return SPA_ERR_ALIGN;
+  return SPA_OK;
+}
+
+// Phase 1 on device: proxy GEMM (fp32 split-K partials) then reduce + cosine + writes.
+int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w_r, const float *pc_read,
+                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s) {
+  const int rows = D.B * D.N;
+  float *part = (float *)at(ws, L.ppart);
+  EpiArgs ea{};
+  SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, D.d, rows, D.r, D.d, part, ea, s));
+  SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, s));
+  return SPA_OK;
+}
+
+// Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N).
+int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const spa_layer_cache *c,
+               const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s) {
+  const int M = D.B * k_per_seq;
+  if (M == 0) return SPA_OK;
+  void *a1 = at(ws, L.a1), *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *b1 = at(ws, L.b1),
+       *z = at(ws, L.z);
+  float *gpart = (float *)at(ws, L.gpart);
+
+  SPA_TRY(launch_rmsnorm(D.dtype, h_in, idx, k_per_seq, D.N, M, D.d, w->g_attn, D.eps, a1, s));
+
+  EpiArgs qkv{};
+  qkv.out = q;
+  qkv.out2 = c->k_cache;
+  qkv.out3 = c->v_cache;
+  qkv.idx = idx;
+  qkv.k_per_seq = k_per_seq;
+  qkv.n_tok = D.N;
+  qkv.dq = D.dq;
+  qkv.dkv = D.dkv;
+  qkv.hkv = D.hkv;
+  qkv.hd = D.hd;
+  const int nqkv = D.dq + 2 * D.dkv;
+  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV), a1, D.d, w->w_qkv, D.d, M, nqkv,
+                      D.d, gpart, qkv, s));
+
+  SPA_TRY(launch_attention(D.dtype, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd, s));
+
+  EpiArgs wo{};
+  wo.out = y;
+  wo.src = h_in;
+  wo.idx = idx;
+  wo.k_per_seq = k_per_seq;
+  wo.n_tok = D.N;
+  wo.ld_src = D.d;
+  wo.ldo = D.d;
+  SPA_TRY(launch_gemm(D.dtype, kEpiResid, plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid), o, D.dq, w->w_o, D.dq, M, D.d,
+                      D.dq, gpart, wo, s));
+
+  SPA_TRY(launch_rmsnorm(D.dtype, y, nullptr, M, M, M, D.d, w->g_ffn, D.eps, b1, s));
+
+  EpiArgs gu{};
+  gu.out = z;
+  gu.f = D.F;
+  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, plan_gemm(D.dtype, M, 2 * D.F, D.d, kEpiSwiGLU), b1, D.d, w->w_gate_up,
+                      D.d, M, 2 * D.F, D.d, gpart, gu, s));
+
+  EpiArgs dn{};
+  dn.out = c->h_cache;
+  dn.src = y;
+  dn.idx = idx;
+  dn.k_per_seq = k_per_seq;
+  dn.n_tok = D.N;
+  dn.ld_src = D.d;
+  dn.ldo = D.d;
+  SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, plan_gemm(D.dtype, M, D.d, D.F, kEpiResidScatter), z, D.F,
+                      w->w_down, D.F, M, D.d, D.F, gpart, dn, s));
+  return SPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *spa_status_string(int status) {
+  switch (status) {
+    case SPA_OK: return "SPA_OK";
+    case SPA_ERR_INVALID_ARG: return "SPA_ERR_INVALID_ARG: null pointer or size out of range";
+    case SPA_ERR_UNSUPPORTED: return "SPA_ERR_UNSUPPORTED: shape or dtype outside the supported set";
+    case SPA_ERR_ALIAS: return "SPA_ERR_ALIAS: an output overlaps an input";
+    case SPA_ERR_ALIGN: return "SPA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case SPA_ERR_WORKSPACE: return "SPA_ERR_WORKSPACE: workspace missing or too small";
+    case SPA_ERR_HIP: return "SPA_ERR_HIP: a HIP launch failed";
+    default: return "unknown spa_status";
+  }
+}
+
+int spa_budget(int32_t n_layers, int32_t l_peak, double rho_peak, double rho_first, double rho_last,
+               int32_t n_tokens, double *rho_out, int32_t *k_out) {
+  if (n_layers < 1 || l_peak < 1 || l_peak > n_layers || n_tokens < 1) return SPA_ERR_INVALID_ARG;
+  const double rs[3] = {rho_peak, rho_first, rho_last};
+  for (double v : rs)
+    if (!(v > 0.0 && v <= 1.0)) return SPA_ERR_INVALID_ARG;
+  for (int l = 1; l <= n_layers; ++l) {
+    double rho;
+    if (l == l_peak) {
+      rho = rho_peak;
+    } else if (l < l_peak) {
+      const double t = (double)(l - l_peak) / (double)(l_peak - 1);
+      rho = (l == 1) ? rho_first : rho_peak * exp(log(rho_first / rho_peak) * t * t);
+    } else {
+      const double t = (double)(l - l_peak) / (double)(n_layers - l_peak);
+      rho = (l == n_layers) ? rho_last : rho_peak * exp(log(rho_last / rho_peak) * t * t);
+    }
+    double kk = floor((double)n_tokens * rho + 1e-9);
+    if (kk < 1.0) kk = 1.0;
+    if (kk > (double)n_tokens) kk = (double)n_tokens;
+    if (rho_out != nullptr) rho_out[l - 1] = rho;
+    if (k_out != nullptr) k_out[l - 1] = (int32_t)kk;
+  }
+  return SPA_OK;
+}
+
+int spa_workspace_bytes(const spa_shape *shape, int32_t k_max, size_t *bytes_out) {
+  Dims D;
+  const int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if (bytes_out == nullptr || k_max < 0 || k_max > D.N) return SPA_ERR_INVALID_ARG;
+  *bytes_out = make_layout(D, k_max).total;
+  return SPA_OK;
+}
+
+int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                   const void *h_in, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if ((st = check_weights(w)) != SPA_OK) return st;
+  if ((st = check_cache(cache, D, h_in)) != SPA_OK) return st;
+  const Layout L = make_layout(D, D.N);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  if ((st = run_identify(D, L, h_in, w->w_r, nullptr, cache->p_cache, nullptr, nullptr, ws, stream)) != SPA_OK)
+    return st;
+  return run_sparse(D, L, w, cache, h_in, nullptr, D.N, ws, stream);
+}
+
+int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                   const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if ((st = check_weights(w)) != SPA_OK) return st;
+  if ((st = check_cache(cache, D, h_in)) != SPA_OK) return st;
+  if (k < 0 || k > D.N) return SPA_ERR_INVALID_ARG;
+  if (policy != SPA_PROXY_WRITE_ALL && policy != SPA_PROXY_WRITE_SELECTED) return SPA_ERR_INVALID_ARG;
+  if (k > 0 && idx_out == nullptr) return SPA_ERR_INVALID_ARG;
+  if ((idx_out && !aligned16(idx_out)) || (scores_out && !aligned16(scores_out))) return SPA_ERR_ALIGN;
+  const size_t xb = (size_t)D.B * D.N * D.d * D.e;
+  if (idx_out && (overlap(idx_out, (size_t)D.B * k * 4, h_in, xb) ||
+                  overlap(idx_out, (size_t)D.B * k * 4, cache->p_cache, (size_t)D.B * D.N * D.r * 4)))
+    return SPA_ERR_ALIAS;
+  const Layout L = make_layout(D, k);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  float *scores = scores_out ? scores_out : (float *)at(ws, L.scores);
+  const bool sel = policy == SPA_PROXY_WRITE_SELECTED;
+  float *pbuf = (float *)at(ws, L.pbuf);
+  if ((st = run_identify(D, L, h_in, w->w_r, cache->p_cache, sel ? nullptr : cache->p_cache, sel ? pbuf : nullptr,
+                         scores, ws, stream)) != SPA_OK)
+    return st;
+  if (k == 0) return SPA_OK;
+  SPA_TRY(launch_topk(scores, D.B, D.N, k, idx_out, stream));
+  if (sel) SPA_TRY(launch_copy_selected(pbuf, cache->p_cache, idx_out, D.B, D.N, k, D.r, stream));
+  return run_sparse(D, L, w, cache, h_in, idx_out, k, ws, stream);
+}
+
+int spa_identify(const spa_shape *shape, const void *h_in, const void *w_r, const float *p_cache, float *p_out,
+                 float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if (h_in == nullptr || w_r == nullptr) return SPA_ERR_INVALID_ARG;
+  if (p_out == nullptr && (p_cache == nullptr || scores_out == nullptr)) return SPA_ERR_INVALID_ARG;
+  if (scores_out != nullptr && p_cache == nullptr) return SPA_ERR_INVALID_ARG;
+  if (!aligned16(h_in) || !aligned16(w_r) || (p_cache && !aligned16(p_cache)) || (p_out && !aligned16(p_out)) ||
+      (scores_out && !aligned16(scores_out)))
+    return SPA_ERR_ALIGN;
+  const size_t pb = (size_t)D.B * D.N * D.r * 4;
+  if (p_out && p_cache && overlap(p_out, pb, p_cache, pb)) return SPA_ERR_ALIAS;
+  const Layout L = make_layout(D, 0);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  return run_identify(D, L, h_in, w_r, p_cache, nullptr, p_out, scores_out, ws, stream);
+}
+
+int spa_topk(int32_t batch, int32_t n, const float *scores, int32_t k, int32_t *idx_out, hipStream_t stream) {
+  if (batch < 1 || n < 1 || k < 0 || k > n) return SPA_ERR_INVALID_ARG;
+  if (n > 16384) return SPA_ERR_UNSUPPORTED;
+  if (scores == nullptr || (k > 0 && idx_out == nullptr)) return SPA_ERR_INVALID_ARG;
+  if (!aligned16(scores) || (idx_out && !aligned16(idx_out))) return SPA_ERR_ALIGN;
+  return hip_status(launch_topk(scores, batch, n, k, idx_out, stream));
+}
+
+int spa_sparse_update(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                      const void *h_in, const int32_t *idx, int32_t k, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  Dims D;
+  int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if ((st = check_weights(w)) != SPA_OK) return st;
+  if ((st = check_cache(cache, D, h_in)) != SPA_OK) return st;
+  if (k < 0 || k > D.N || (k > 0 && idx == nullptr)) return SPA_ERR_INVALID_ARG;
+  if (idx && !aligned16(idx)) return SPA_ERR_ALIGN;
+  const Layout L = make_layout(D, k);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  return run_sparse(D, L, w, cache, h_in, idx, k, ws, stream);
+}
+
+int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const void *k_cache, const void *v_cache,
+               void *o_out, hipStream_t stream) {
+  Dims D;
+  int st = check_shape(shape, &D);
+  if (st != SPA_OK) return st;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || o_out == nullptr || m_per_seq < 0)
+    return SPA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_out)) return SPA_ERR_ALIGN;
+  const size_t ob = (size_t)D.B * m_per_seq * D.dq * D.e;
+  const size_t kvb = (size_t)D.B * D.hkv * D.N * D.hd * D.e;
+  if (overlap(o_out, ob, q, ob) || overlap(o_out, ob, k_cache, kvb) || overlap(o_out, ob, v_cache, kvb))
+    return SPA_ERR_ALIAS;
+  return hip_status(
+      launch_attention(D.dtype, q, k_cache, v_cache, o_out, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd, stream));
+}
+
+}  // extern "C"

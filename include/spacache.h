@@ -1,0 +1,156 @@
+/*
+ * spacache.h -- C ABI of libspacache, the SPA-Cache per-layer decoding step on MI355X (gfx950).
+ *
+ * Method: "SPA-Cache: Singular Proxies for Adaptive Caching in Diffusion Language Models"
+ * (arXiv 2602.02544). Citations name the page and section:
+ *   [PN]  papernotes.org notes (ICML 2026): "方法详解 / 整体框架" (Algorithm 1, phases 1-3),
+ *         "关键设计 2" (singular proxy W_r = Lambda_r V_r^T), "关键设计 3" (rho(l) equation).
+ *   [GS]  gist.science technical summary, "Methodology: SPA-Cache", parts 1-3.
+ *
+ * Conventions shared by every entry point
+ *   - Memory. Every pointer except those of spa_budget and spa_workspace_bytes is a DEVICE pointer
+ *     owned by the caller; the library never allocates, frees or keeps a pointer after returning.
+ *     Every device pointer must be 16-byte aligned (SPA_ERR_ALIGN otherwise).
+ *   - Layouts. Row-major everywhere. Weight matrices are [out][in], so y = x W^T.
+ *       X (h_in)      B x N x d            dtype
+ *       K^c, V^c      B x H_kv x N x hd    dtype (head-major: one head's keys are contiguous)
+ *       H^c           B x N x d            dtype (the layer output)
+ *       P^c           B x N x r            float32 (the proxy cache)
+ *       scores        B x N                float32
+ *       idx           B x k                int32, ascending within each sequence
+ *   - dtype. SPA_BF16 (bfloat16 storage, fp32 accumulation) or SPA_F32 (fp32 throughout).
+ *   - Streams. Calls only enqueue work on `stream` (0 = the null stream): no host synchronisation,
+ *     no allocation, so a sequence of calls can be captured in a HIP graph. k is a host integer.
+ *   - Errors. Every call validates its arguments before any launch and returns a spa_status;
+ *     nothing aborts or throws. SPA_ERR_HIP reports a launch failure; faults inside kernels surface
+ *     at the caller's next synchronisation.
+ *   - Threads. No global mutable state: concurrent calls on different streams with disjoint
+ *     buffers are safe.
+ *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0; d_ffn % 16 == 0; head_dim in {64, 128};
+ *     n_q_heads % n_kv_heads == 0; 16 <= r <= 1024, r % 16 == 0, r <= min(d, d_kv).
+ */
+#ifndef SPACACHE_H
+#define SPACACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPA_OK = 0,
+  SPA_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size, k out of range      */
+  SPA_ERR_UNSUPPORTED = -2,  /* a shape or dtype outside the supported set above                  */
+  SPA_ERR_ALIAS = -3,        /* an output overlaps an input it must not overlap                    */
+  SPA_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned                            */
+  SPA_ERR_WORKSPACE = -5,    /* workspace pointer null or smaller than spa_workspace_bytes()       */
+  SPA_ERR_HIP = -6           /* a HIP launch returned an error                                     */
+} spa_status;
+
+typedef enum { SPA_F32 = 0, SPA_BF16 = 1 } spa_dtype;
+
+/* Which rows the proxy cache P^c takes after a cached step ([PN] 整体框架 Phase 1 compares with
+ * "the proxy cached at the previous step"): ALL = every token's new proxy (default), SELECTED =
+ * only the recomputed rows, so P^c always matches the inputs of the cached K/V/H rows. */
+typedef enum { SPA_PROXY_WRITE_ALL = 0, SPA_PROXY_WRITE_SELECTED = 1 } spa_proxy_policy;
+
+typedef struct {
+  int32_t batch;       /* B: independent sequences                                   */
+  int32_t n_tokens;    /* N                                                          */
+  int32_t d_model;     /* d                                                          */
+  int32_t n_q_heads;   /* H_q                                                        */
+  int32_t n_kv_heads;  /* H_kv (grouped-query attention when < H_q)                  */
+  int32_t head_dim;    /* hd                                                         */
+  int32_t d_ffn;       /* F: SwiGLU hidden size                                      */
+  int32_t rank;        /* r: rows of the singular proxy W_r                          */
+  int32_t dtype;       /* spa_dtype                                                  */
+  float norm_eps;      /* RMSNorm epsilon                                            */
+} spa_shape;
+
+/* Layer weights (device, read-only). The block is pre-norm: RMSNorm(g_attn) -> QKV -> attention ->
+ * W_o -> residual -> RMSNorm(g_ffn) -> SwiGLU -> W_down -> residual. */
+typedef struct {
+  const void *w_r;        /* r x d: Lambda_r V_r^T of W_v diag(g_attn) ([PN] 关键设计 2)          */
+  const void *w_qkv;      /* (d_q + 2 d_kv) x d: rows [W_q; W_k; W_v]                             */
+  const void *w_o;        /* d x d_q                                                              */
+  const void *w_gate_up;  /* 2F x d: rows [W_gate; W_up]                                          */
+  const void *w_down;     /* d x F                                                                */
+  const void *g_attn;     /* d: attention RMSNorm gain                                            */
+  const void *g_ffn;      /* d: FFN RMSNorm gain                                                  */
+} spa_layer_weights;
+
+/* Per-layer caches (device, read-write), owned by the caller across steps. */
+typedef struct {
+  void *k_cache;   /* B x H_kv x N x hd */
+  void *v_cache;   /* B x H_kv x N x hd */
+  void *h_cache;   /* B x N x d: the layer output; rows outside the update set keep their values */
+  float *p_cache;  /* B x N x r */
+} spa_layer_cache;
+
+/* Per-layer row budget ([PN] 关键设计 3, the piecewise-Gaussian rho(l)). Host only.
+ * rho(l) = rho_p exp(ln(rho_1/rho_p) ((l - l_p)/(l_p - 1))^2) for l <= l_p, and the mirrored branch
+ * rho_p exp(ln(rho_L/rho_p) ((l - l_p)/(L - l_p))^2) for l > l_p; layers are 1-based and the peak
+ * and endpoints are exact. k_l = clamp(floor(N rho(l) + 1e-9), 1, N).
+ * rho_out (double[n_layers]) and k_out (int32[n_layers]) are host arrays; either may be NULL.
+ * SPA_ERR_INVALID_ARG unless n_layers >= 1, 1 <= l_peak <= n_layers, n_tokens >= 1 and every
+ * budget lies in (0, 1]. */
+int spa_budget(int32_t n_layers, int32_t l_peak, double rho_peak, double rho_first,
+               double rho_last, int32_t n_tokens, double *rho_out, int32_t *k_out);
+
+/* Device workspace needed by calls on `shape` that update at most k_max rows per sequence
+ * (spa_layer_full needs k_max >= N). Host only; writes *bytes_out. */
+int spa_workspace_bytes(const spa_shape *shape, int32_t k_max, size_t *bytes_out);
+
+/* Warm-up step t = 0 and the vanilla full recompute ([PN] 整体框架 with every token updated):
+ * fills K^c, V^c, H^c from the full block over all N tokens and sets P^c = X W_r^T.
+ * h_in must not overlap h_cache (SPA_ERR_ALIAS). */
+int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                   const void *h_in, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* One cached SPA-Cache layer step t >= 1 ([PN] 整体框架 phases 1-3; [GS] parts 1 and 3):
+ *  1. P = X W_r^T; s_i = <p_i, p^c_i> / (max(|p_i|,1e-8) max(|p^c_i|,1e-8)); I = the k least similar
+ *     tokens of each sequence (ties to the lower index, NaN first), ascending; P^c updated by policy.
+ *  2. Q/K/V for rows in I; K, V scattered into K^c, V^c; the k queries attend to all N cached keys.
+ *  3. W_o + residual, RMSNorm, SwiGLU FFN + residual on those rows, scattered into H^c[I].
+ * k in [0, N]. idx_out (B x k int32) receives I; scores_out (B x N float32) may be NULL.
+ * h_in must not overlap h_cache. */
+int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                   const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Phase 1 scores only ([PN] 整体框架 Phase 1; [GS] part 1): p_out = X W_r^T (B x N x r float32) and,
+ * when p_cache is not NULL, scores_out = cosine(p, p^c) (B x N). Never writes p_cache.
+ * p_out may be NULL when only scores are wanted; scores_out may be NULL when p_cache is. */
+int spa_identify(const spa_shape *shape, const void *h_in, const void *w_r, const float *p_cache,
+                 float *p_out, float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Top-k least similar ([PN] 整体框架 Phase 1): for each of `batch` rows of `scores` (n floats),
+ * the k indices of the smallest scores under the order (value, index), NaN lowest, -0 = +0,
+ * written ascending to idx_out (batch x k). 1 <= n <= 16384, 0 <= k <= n. No workspace. */
+int spa_topk(int32_t batch, int32_t n, const float *scores, int32_t k, int32_t *idx_out,
+             hipStream_t stream);
+
+/* Phases 2-3 for a given update set idx (B x k int32, entries in [0, N); ascending order is not
+ * required; a repeated index writes identical rows twice). Rows outside idx keep their cached
+ * K/V/H values; P^c is not touched. Entries outside [0, N) are skipped by every write. */
+int spa_sparse_update(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                      const void *h_in, const int32_t *idx, int32_t k, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Phase 2b alone ([PN] 整体框架 Phase 2): q (M x H_q x hd, dtype, M = B * m_per_seq rows, the first
+ * m_per_seq belonging to sequence 0, ...) attends to every key of its sequence's K^c/V^c with
+ * scale 1/sqrt(hd), no mask; o_out (M x H_q x hd, dtype). */
+int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const void *k_cache,
+               const void *v_cache, void *o_out, hipStream_t stream);
+
+/* Human-readable name of a spa_status value. */
+const char *spa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPACACHE_H */

@@ -41,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "round_bf16", "store", "budget", "singular_proxy", "proxy", "cosine", "order_key",
-    "select_topk", "rmsnorm", "silu", "attention", "full_layer", "warmup", "sparse_update",
+    "select_topk", "rmsnorm", "silu", "attention", "full_layer", "kv_project", "warmup", "sparse_update",
     "cached_layer_step", "LayerCache", "POLICY_ALL", "POLICY_SELECTED",
 ]
 
@@ -243,6 +243,23 @@ def full_layer(x: np.ndarray, w: Dict[str, np.ndarray], head_dim: int, eps: floa
         z = silu(bb @ np.asarray(w["w_gate"], np.float64).T) * (bb @ np.asarray(w["w_up"], np.float64).T)
         hc[bi] = store(y + z @ np.asarray(w["w_down"], np.float64).T, dtype)
     return kc, vc, hc
+
+
+def kv_project(x: np.ndarray, w: Dict[str, np.ndarray], head_dim: int, eps: float, dtype: str = "f64"):
+    """K and V of every token (the cache contents a full forward leaves), rounded to `dtype`.
+
+    The same arithmetic as the K/V part of full_layer, without the queries, attention and FFN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    b, n, _ = x.shape
+    hkv = w["w_k"].shape[0] // head_dim
+    kc = np.empty((b, hkv, n, head_dim))
+    vc = np.empty((b, hkv, n, head_dim))
+    for bi in range(b):
+        a = rmsnorm(x[bi], w["g_attn"], eps)
+        kc[bi] = store((a @ np.asarray(w["w_k"], np.float64).T).reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
+        vc[bi] = store((a @ np.asarray(w["w_v"], np.float64).T).reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
+    return kc, vc
 
 
 def warmup(x: np.ndarray, w: Dict[str, np.ndarray], w_r: np.ndarray, head_dim: int, eps: float,

@@ -98,3 +98,13 @@ def test_full_layer_matches_torch_composition(shape):
     assert np.allclose(kc, rk, rtol=1e-12, atol=1e-12)
     assert np.allclose(vc, rv, rtol=1e-12, atol=1e-12)
     assert np.allclose(h, rh, rtol=1e-12, atol=1e-12)
+
+
+def test_kv_project_matches_full_layer():
+    shape = synth.LayerShape(2, 19, 64, 4, 2, 16, 48, 8, "f32")
+    w = synth.random_weights(shape, seed=8, std=0.1, gains="random")
+    x = synth.random_hidden(shape, seed=9)
+    for dtype in ("f64", "bf16"):
+        kc, vc, _ = oracle.full_layer(x, w, shape.head_dim, 1e-6, dtype)
+        k2, v2 = oracle.kv_project(x, w, shape.head_dim, 1e-6, dtype)
+        assert np.array_equal(kc, k2) and np.array_equal(vc, v2)
