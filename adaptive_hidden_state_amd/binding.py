@@ -19,8 +19,8 @@ SPA_F32, SPA_BF16 = 0, 1
 SPA_PROXY_WRITE_ALL, SPA_PROXY_WRITE_SELECTED = 0, 1
 
 # Every symbol include/spacache.h declares.
-EXPORTS = ("spa_budget", "spa_workspace_bytes", "spa_layer_full", "spa_layer_step", "spa_identify",
-           "spa_topk", "spa_sparse_update", "spa_attend", "spa_status_string")
+EXPORTS = ("spa_budget", "spa_workspace_bytes", "spa_layer_full", "spa_layer_step", "spa_layer_step_timed",
+           "spa_identify", "spa_topk", "spa_sparse_update", "spa_attend", "spa_status_string")
 
 
 class SpaError(RuntimeError):
@@ -47,6 +47,11 @@ class spa_layer_cache(ctypes.Structure):
                 ("p_cache", ctypes.c_void_p)]
 
 
+class spa_timing(ctypes.Structure):
+    _fields_ = [("marks", ctypes.c_void_p), ("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("names", ctypes.c_void_p)]
+
+
 _lib_handle: Optional[ctypes.CDLL] = None
 
 
@@ -65,6 +70,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spa_workspace_bytes": ([P, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "spa_layer_full": ([P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_layer_step": ([P, P, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
+        "spa_layer_step_timed": ([P, P, P, P, I32, I32, P, P, P, SZ, P, P], ctypes.c_int),
         "spa_identify": ([P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_topk": ([I32, I32, P, I32, P, P], ctypes.c_int),
         "spa_sparse_update": ([P, P, P, P, P, I32, P, SZ, P], ctypes.c_int),
@@ -211,6 +217,56 @@ def spa_layer_step(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, po
                                          int(k), int(policy), _ptr(idx_out, torch.int32, "idx_out"),
                                          _ptr(scores_out, torch.float32, "scores_out"), wp, wb, _stream(stream)),
            "spa_layer_step")
+
+
+class HipEvents:
+    """`n` HIP timing events (created through the HIP runtime) for spa_layer_step_timed."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.n = n
+        self.events = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+        self.names = (ctypes.c_char_p * max(n - 1, 1))()
+
+    def timing(self) -> spa_timing:
+        return spa_timing(ctypes.cast(self.events, ctypes.c_void_p), self.n, 0,
+                          ctypes.cast(self.names, ctypes.c_void_p))
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float(0.0)
+        if self.hip.hipEventSynchronize(ctypes.c_void_p(self.events[j])) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.events[i]),
+                                        ctypes.c_void_p(self.events[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(ctypes.c_void_p(self.events[i]))
+
+
+def spa_layer_step_timed(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, policy: int, idx_out,
+                         scores_out, ws, events: HipEvents, stream=None):
+    """spa_layer_step with an event after every kernel; returns [(kernel name, duration ms), ...]."""
+    import torch
+    tdt = torch_dtype(shape.dtype)
+    s = make_shape(shape)
+    wp, wb = _ws(ws)
+    ws_ = _weights_struct(w, tdt)
+    cs = _cache_struct(cache, tdt)
+    t = events.timing()
+    _check(load_library().spa_layer_step_timed(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs),
+                                               _ptr(h_in, tdt, "h_in"), int(k), int(policy),
+                                               _ptr(idx_out, torch.int32, "idx_out"),
+                                               _ptr(scores_out, torch.float32, "scores_out"), wp, wb,
+                                               _stream(stream), ctypes.byref(t)), "spa_layer_step_timed")
+    return [(events.names[i].decode(), events.elapsed_ms(i, i + 1)) for i in range(t.count - 1)]
 
 
 def spa_identify(shape, h_in, w_r, p_cache, p_out, scores_out, ws, stream=None):

@@ -16,31 +16,34 @@ template <bool BF16> struct AFrag;
 template <> struct AFrag<true> { typedef u32x4 type; };
 template <> struct AFrag<false> { typedef float type; };
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ q, const T *__restrict__ kc,
-                                                        const T *__restrict__ vc, T *__restrict__ o, int m_per_seq,
-                                                        int n_tok, int hq, int hkv, float scale_log2) {
+template <typename T, int HD, int QW>
+__global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict__ q, const T *__restrict__ kc,
+                                                            const T *__restrict__ vc, T *__restrict__ o,
+                                                            int m_per_seq, int n_tok, int hq, int hkv,
+                                                            float scale_log2) {
   constexpr bool BF = sizeof(T) == 2;
-  constexpr int KT = 64;                                // keys per tile
-  constexpr int KROWB = HD * (int)sizeof(T) + 16;       // K tile row stride (bytes)
+  constexpr int NT = 64 * QW;
+  constexpr int KT = 64;                                      // keys per tile
+  constexpr int KROWB = HD * (int)sizeof(T) + 16;             // K tile row stride (bytes)
   constexpr int VROWB = KT * (int)sizeof(T) + (BF ? 8 : 16);  // V^T tile row stride (bytes)
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int CPR = HD / VEC;                          // 16-byte chunks per key row
-  constexpr int KCH = KT * CPR / 256;                    // chunks per thread per tile
+  constexpr int CPR = HD / VEC;                               // 16-byte chunks per key row
+  constexpr int KCH = KT * CPR / NT;                          // chunks per thread per tile (each of K, V)
   constexpr int QSTEPS = BF ? HD / 32 : HD / 4;
   constexpr int KSTEP_B = BF ? 64 : 16;
   constexpr int LANE_B = BF ? 16 : 4;
   constexpr int HB = HD / 16;
-  static_assert(KT * CPR % 256 == 0, "tile load split");
+  constexpr int PF = 2;                                       // key tiles in flight in registers
+  static_assert(KT * CPR % NT == 0, "tile load split");
   typedef typename AFrag<BF>::type FragT;
 
-  __shared__ __attribute__((aligned(16))) char ks[KT * KROWB];
-  __shared__ __attribute__((aligned(16))) char vts[HD * VROWB];
+  __shared__ __attribute__((aligned(16))) char ks[2][KT * KROWB];
+  __shared__ __attribute__((aligned(16))) char vts[2][HD * VROWB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.z, h = blockIdx.y;
   const int g = h / (hq / hkv);
-  const int m0 = blockIdx.x * 64 + wave * 16;
+  const int m0 = blockIdx.x * (16 * QW) + wave * 16;
   const int ldq = hq * HD;
 
   // Q fragments: B operand of S^T = K Q^T (column = query lane&15, k = head dim).
@@ -49,11 +52,11 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ q,
     const int qrow = min(m0 + (lane & 15), m_per_seq - 1);
     const T *qp = q + ((size_t)b * m_per_seq + qrow) * ldq + (size_t)h * HD;
 #pragma unroll
-    for (int s = 0; s < QSTEPS; ++s) {
+    for (int st = 0; st < QSTEPS; ++st) {
       if constexpr (BF)
-        qf[s] = ld16(qp + s * 32 + (lane >> 4) * 8);
+        qf[st] = ld16(qp + st * 32 + (lane >> 4) * 8);
       else
-        qf[s] = qp[s * 4 + (lane >> 4)];
+        qf[st] = qp[st * 4 + (lane >> 4)];
     }
   }
 
@@ -66,61 +69,54 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ q,
   for (int i = 0; i < HB; ++i) oacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  u32x4 rk[KCH], rv[KCH];
-  auto gload = [&](int t) {
+  u32x4 rk[PF][KCH], rv[PF][KCH];
+  auto gload = [&](int t, u32x4 *xk, u32x4 *xv) {
     const int key0 = t * KT;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * NT;
       const int row = c / CPR, col = c % CPR;
       const int key = min(key0 + row, n_tok - 1);
-      rk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
+      xk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
     }
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * NT;
       const int row = c % KT, col = c / KT;
       const int key = min(key0 + row, n_tok - 1);
-      rv[j] = ld16(reinterpret_cast<const char *>(vbase + (size_t)key * HD) + col * 16);
+      xv[j] = ld16(reinterpret_cast<const char *>(vbase + (size_t)key * HD) + col * 16);
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf, const u32x4 *xk, const u32x4 *xv) {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * NT;
       const int row = c / CPR, col = c % CPR;
-      st16(ks + row * KROWB + col * 16, rk[j]);
+      st16(ks[buf] + row * KROWB + col * 16, xk[j]);
     }
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * 256;
+      const int c = tid + j * NT;
       const int key = c % KT, e0 = (c / KT) * VEC;
       if constexpr (BF) {
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          *reinterpret_cast<uint16_t *>(vts + (e0 + u) * VROWB + key * 2) =
-              (uint16_t)(rv[j][u >> 1] >> (16 * (u & 1)));
+          *reinterpret_cast<uint16_t *>(vts[buf] + (e0 + u) * VROWB + key * 2) =
+              (uint16_t)(xv[j][u >> 1] >> (16 * (u & 1)));
       } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) *reinterpret_cast<uint32_t *>(vts + (e0 + u) * VROWB + key * 4) = rv[j][u];
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<uint32_t *>(vts[buf] + (e0 + u) * VROWB + key * 4) = xv[j][u];
       }
     }
   };
 
-  const int ntiles = (n_tok + KT - 1) / KT;
-  gload(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (t + 1 < ntiles) gload(t + 1);
-
+  auto compute = [&](int t, int buf) {
     // S^T blocks: rows = keys kb*16 + 4*(lane>>4) + i, column = query lane & 15
     floatx4 s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const char *krow = ks + (kb * 16 + (lane & 15)) * KROWB + (lane >> 4) * LANE_B;
+      const char *krow = ks[buf] + (kb * 16 + (lane & 15)) * KROWB + (lane >> 4) * LANE_B;
 #pragma unroll
       for (int st = 0; st < QSTEPS; ++st)
         s[kb] = mfma16(*reinterpret_cast<const FragT *>(krow + st * KSTEP_B), qf[st], s[kb]);
@@ -166,7 +162,7 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ q,
         const int c1 = c0 + 32;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          const char *vrow = vts + (hb * 16 + (lane & 15)) * VROWB;
+          const char *vrow = vts[buf] + (hb * 16 + (lane & 15)) * VROWB;
           const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
           const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
@@ -181,10 +177,33 @@ __global__ __launch_bounds__(256) void attention_kernel(const T *__restrict__ q,
           const int c = (kb * 16 + (lane >> 4) * 4 + i) * 4;
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
-            const float vf = *reinterpret_cast<const float *>(vts + (hb * 16 + (lane & 15)) * VROWB + c);
+            const float vf = *reinterpret_cast<const float *>(vts[buf] + (hb * 16 + (lane & 15)) * VROWB + c);
             oacc[hb] = mfma16(vf, s[kb][i], oacc[hb]);
           }
         }
+    }
+  };
+
+  const int ntiles = (n_tok + KT - 1) / KT;
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < ntiles) gload(u, rk[u], rv[u]);
+  lstore(0, rk[0], rv[0]);
+  if (PF < ntiles) gload(PF, rk[0], rv[0]);
+  __syncthreads();
+  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int t = t0 + u;
+      if (t < ntiles) {
+        compute(t, t & 1);
+        const int nslot = (u + 1) % PF;
+        if (t + 1 < ntiles) {
+          lstore((t + 1) & 1, rk[nslot], rv[nslot]);
+          if (t + 1 + PF < ntiles) gload(t + 1 + PF, rk[nslot], rv[nslot]);
+        }
+        __syncthreads();
+      }
     }
   }
 
@@ -213,9 +232,17 @@ template <typename T, int HD>
 static hipError_t run_attention(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
                                 int n_tok, int hq, int hkv, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  dim3 grid((m_per_seq + 63) / 64, hq, batch);
-  hipLaunchKernelGGL((attention_kernel<T, HD>), grid, dim3(256), 0, s, (const T *)q, (const T *)kc,
-                     (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, scale_log2);
+  // 64 queries per workgroup when that already fills the chip, else 32
+  const long wg64 = (long)((m_per_seq + 63) / 64) * hq * batch;
+  if (wg64 >= 256) {
+    dim3 grid((m_per_seq + 63) / 64, hq, batch);
+    hipLaunchKernelGGL((attention_kernel<T, HD, 4>), grid, dim3(256), 0, s, (const T *)q, (const T *)kc,
+                       (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, scale_log2);
+  } else {
+    dim3 grid((m_per_seq + 31) / 32, hq, batch);
+    hipLaunchKernelGGL((attention_kernel<T, HD, 2>), grid, dim3(128), 0, s, (const T *)q, (const T *)kc,
+                       (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, scale_log2);
+  }
   return hipGetLastError();
 }
 

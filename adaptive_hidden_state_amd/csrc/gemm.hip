@@ -76,7 +76,7 @@ template <bool BF16> struct Frag;
 template <> struct Frag<true> { typedef u32x4 type; };
 template <> struct Frag<false> { typedef float type; };
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int KIND>
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int KIND, int PF>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     const T *__restrict__ A, int lda, const T *__restrict__ W, int ldw, int M, int N, int K, int tiles_m,
     int tiles_n, int k_split, float *__restrict__ part, EpiArgs ea) {
@@ -94,6 +94,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tiles are made of 16x16 blocks");
   static_assert(KIND != kEpiSwiGLU || (WTN % 32 == 0), "gate/up pairs must stay inside a wave");
+  static_assert(PF >= 1 && PF <= 4, "prefetch depth");
   typedef typename Frag<IS_BF16>::type FragT;
 
   __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
@@ -132,20 +133,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
     b_k[j] = k0 + col * VEC;
   }
 
-  u32x4 ra[A_PER], rb[B_PER];
+  // Register ring of PF K slabs in flight: slab kt lives in slot kt % PF from its load until it is
+  // written to LDS one iteration before it is used.
+  u32x4 ra[PF][A_PER], rb[PF][B_PER];
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto gload = [&](int kt) {
+  auto gload = [&](int kt, u32x4 *xa, u32x4 *xb) {
     const int kb = kt * BK;
 #pragma unroll
-    for (int j = 0; j < A_PER; ++j) ra[j] = (a_k[j] + kb < k1) ? ld16(a_src[j] + kb * sizeof(T)) : zero;
+    for (int j = 0; j < A_PER; ++j) xa[j] = (a_k[j] + kb < k1) ? ld16(a_src[j] + kb * sizeof(T)) : zero;
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) rb[j] = (b_k[j] + kb < k1) ? ld16(b_src[j] + kb * sizeof(T)) : zero;
+    for (int j = 0; j < B_PER; ++j) xb[j] = (b_k[j] + kb < k1) ? ld16(b_src[j] + kb * sizeof(T)) : zero;
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const u32x4 *xa, const u32x4 *xb) {
 #pragma unroll
-    for (int j = 0; j < A_PER; ++j) st16(&lds[buf][a_dst[j]], ra[j]);
+    for (int j = 0; j < A_PER; ++j) st16(&lds[buf][a_dst[j]], xa[j]);
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) st16(&lds[buf][b_dst[j]], rb[j]);
+    for (int j = 0; j < B_PER; ++j) st16(&lds[buf][b_dst[j]], xb[j]);
   };
 
   floatx4 acc[FM][FN];
@@ -154,32 +157,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+    if (u < nk) gload(u, ra[u], rb[u]);
   if (nk > 0) {
-    gload(0);
-    lstore(0);
+    lstore(0, ra[0], rb[0]);
+    if (PF < nk) gload(PF, ra[0], rb[0]);
   }
   __syncthreads();
 
   const int frag_off = (lane & 15) * ROWB + (lane >> 4) * LANE_B;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char *As = &lds[cur][(wm * WTM) * ROWB + frag_off];
-    const char *Bs = &lds[cur][BM * ROWB + (wn * WTN) * ROWB + frag_off];
+  for (int kt0 = 0; kt0 < nk; kt0 += PF) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      FragT af[FM], bfr[FN];
+    for (int u = 0; u < PF; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nk) {
+        const int cur = kt & 1;
+        const char *As = &lds[cur][(wm * WTM) * ROWB + frag_off];
+        const char *Bs = &lds[cur][BM * ROWB + (wn * WTN) * ROWB + frag_off];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const FragT *>(As + i * 16 * ROWB + ks * KSTEP_B);
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          FragT af[FM], bfr[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const FragT *>(Bs + j * 16 * ROWB + ks * KSTEP_B);
+          for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const FragT *>(As + i * 16 * ROWB + ks * KSTEP_B);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int j = 0; j < FN; ++j)
+            bfr[j] = *reinterpret_cast<const FragT *>(Bs + j * 16 * ROWB + ks * KSTEP_B);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+        }
+        const int nslot = (u + 1) % PF;
+        if (kt + 1 < nk) {
+          lstore(cur ^ 1, ra[nslot], rb[nslot]);
+          if (kt + 1 + PF < nk) gload(kt + 1 + PF, ra[nslot], rb[nslot]);
+        }
+        __syncthreads();
+      }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
   }
 
   const int row0 = tm * BM + wm * WTM + (lane >> 4) * 4;
@@ -255,30 +271,43 @@ constexpr int kTargetWGs = 256;  // one workgroup per CU of an MI355X
 struct TileCfg {
   int bm, bn;
 };
-// cfg 0: fp32, 64x64 (2x2 waves); cfg 1: bf16 128x128 (2x2 waves of 64x64); cfg 2: bf16 64x128 (1x4)
-constexpr TileCfg kTiles[3] = {{64, 64}, {128, 128}, {64, 128}};
+// 0: fp32 64x64 (2x2 waves); 1: bf16 128x128 (2x2 waves of 64x64); 2: bf16 64x128 (1x4 waves of 64x32);
+// 3: bf16 128x64 (2x2 waves of 64x32)
+constexpr TileCfg kTiles[4] = {{64, 64}, {128, 128}, {64, 128}, {128, 64}};
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
 }  // namespace
 
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
   GemmPlan p{};
-  p.cfg = dtype == kF32 ? 0 : (M >= 128 ? 1 : 2);
+  if (dtype == kF32) {
+    p.cfg = 0;
+  } else if (M <= 64) {
+    p.cfg = 2;
+  } else {
+    // the biggest tile that still gives every CU a workgroup; otherwise the one with most tiles
+    const int t1 = ceil_div(M, 128) * ceil_div(N, 128);
+    const int t3 = ceil_div(M, 128) * ceil_div(N, 64);
+    p.cfg = (t1 >= kTargetWGs || t3 <= t1) ? 1 : 3;
+  }
   p.bm = kTiles[p.cfg].bm;
   p.bn = kTiles[p.cfg].bn;
-  p.tiles_m = (M + p.bm - 1) / p.bm;
-  p.tiles_n = (N + p.bn - 1) / p.bn;
+  p.tiles_m = ceil_div(M, p.bm);
+  p.tiles_n = ceil_div(N, p.bn);
   const int bk = dtype == kF32 ? 32 : 64;
   const int tiles = p.tiles_m * p.tiles_n;
   int splits = 1;
-  if (kind == kEpiPartial || tiles < kTargetWGs / 2) {
-    const int max_splits = K / (bk * 4) > 1 ? K / (bk * 4) : 1;
-    splits = (kTargetWGs + tiles - 1) / tiles;
+  if (kind == kEpiPartial || tiles < kTargetWGs / 4) {
+    int max_splits = K / (bk * 4) > 1 ? K / (bk * 4) : 1;
+    if (max_splits > 16) max_splits = 16;
+    splits = ceil_div(kTargetWGs, tiles);
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
   }
-  int ks = (K + splits - 1) / splits;
-  ks = (ks + bk - 1) / bk * bk;
+  int ks = ceil_div(K, splits);
+  ks = ceil_div(ks, bk) * bk;
   p.k_split = ks;
-  p.splits = (K + ks - 1) / ks;
+  p.splits = ceil_div(K, ks);
   if (p.splits < 1) p.splits = 1;
   return p;
 }
@@ -290,10 +319,11 @@ size_t gemm_partial_bytes(const GemmPlan &p, int M, int N) {
 template <typename T, int BM, int BN, int WMv, int WNv, int KIND>
 static hipError_t run_gemm(const GemmPlan &p, const void *A, int lda, const void *W, int ldw, int M, int N,
                            int K, float *part, const EpiArgs &ea, hipStream_t s) {
+  constexpr int PF = 3;
   const bool use_part = (KIND == kEpiPartial) || p.splits > 1;
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
   EpiArgs e = ea;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WMv, WNv, KIND>), dim3(grid), dim3(64 * WMv * WNv), 0, s,
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WMv, WNv, KIND, PF>), dim3(grid), dim3(64 * WMv * WNv), 0, s,
                      (const T *)A, lda, (const T *)W, ldw, M, N, K, p.tiles_m, p.tiles_n, p.k_split,
                      use_part ? part : nullptr, e);
   hipError_t err = hipGetLastError();
@@ -307,10 +337,14 @@ static hipError_t run_gemm(const GemmPlan &p, const void *A, int lda, const void
 template <typename T, int KIND>
 static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void *W, int ldw, int M, int N, int K,
                           float *part, const EpiArgs &ea, hipStream_t s) {
-  switch (p.cfg) {
-    case 0: return run_gemm<T, 64, 64, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
-    case 1: return run_gemm<T, 128, 128, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
-    default: return run_gemm<T, 64, 128, 1, 4, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+  if constexpr (sizeof(T) == 4) {
+    return run_gemm<T, 64, 64, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+  } else {
+    switch (p.cfg) {
+      case 1: return run_gemm<T, 128, 128, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+      case 3: return run_gemm<T, 128, 64, 2, 2, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+      default: return run_gemm<T, 64, 128, 1, 4, KIND>(p, A, lda, W, ldw, M, N, K, part, ea, s);
+    }
   }
 }
 
@@ -330,11 +364,7 @@ static hipError_t run_kind(int kind, const GemmPlan &p, const void *A, int lda, 
 hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W, int ldw,
                        int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (dtype == kF32) {
-    // fp32 uses the single 64x64 configuration
-    GemmPlan p = plan;
-    return run_kind<float>(kind, p, A, lda, W, ldw, M, N, K, part, ea, s);
-  }
+  if (dtype == kF32) return run_kind<float>(kind, plan, A, lda, W, ldw, M, N, K, part, ea, s);
   return run_kind<bf16_t>(kind, plan, A, lda, W, ldw, M, N, K, part, ea, s);
 }
 

@@ -12,6 +12,7 @@ namespace spa {
 // partial-sum reduce + cosine + proxy-cache write; one wave per token row
 // ---------------------------------------------------------------------------------------------
 constexpr int kMaxRankPerLane = 16;  // r <= 1024
+constexpr int kMaxSplits = 16;       // the proxy GEMM never splits K more than this
 
 __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
                                                            int r, const float *pc_read, float *pc_write,
@@ -28,7 +29,11 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
     const int col = lane + 64 * c;
     float v = 0.f;
     if (col < r) {
-      for (int s = 0; s < splits; ++s) v += part[s * plane + base + col];
+      float ps[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) ps[s] = s < splits ? part[s * plane + base + col] : 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) v += ps[s];
       n1 += v * v;
       if (pc_read != nullptr) {
         const float w = pc_read[base + col];
@@ -214,6 +219,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ src,
                                                       int k_per_seq, int n_tok, int rows, int d,
                                                       const T *__restrict__ g, float eps, T *__restrict__ dst) {
   constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int MAXV = 16;  // 16-byte vectors per lane held in registers: d <= 1024 * VEC
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= rows) return;
@@ -226,22 +232,33 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ src,
   const T *x = src + srow * d;
   T *y = dst + (size_t)m * d;
   const int nvec = d / VEC;
+  u32x4 xv[MAXV];
   float ss = 0.f;
-  for (int v = lane; v < nvec; v += 64) {
-    float f[VEC];
-    unpack16(ld16(x + v * VEC), f, (const T *)nullptr);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) ss += f[j] * f[j];
+  for (int j = 0; j < MAXV; ++j) {
+    const int v = lane + 64 * j;
+    xv[j] = v < nvec ? ld16(x + v * VEC) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int j = 0; j < MAXV; ++j) {
+    float f[VEC];
+    unpack16(xv[j], f, (const T *)nullptr);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += f[e] * f[e];
   }
   ss = wave_sum(ss);
   const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int v = lane; v < nvec; v += 64) {
-    float f[VEC], w[VEC];
-    unpack16(ld16(x + v * VEC), f, (const T *)nullptr);
-    unpack16(ld16(g + v * VEC), w, (const T *)nullptr);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) f[j] = f[j] * rinv * w[j];
-    st16(y + v * VEC, pack16(f, (const T *)nullptr));
+  for (int j = 0; j < MAXV; ++j) {
+    const int v = lane + 64 * j;
+    if (v < nvec) {
+      float f[VEC], w[VEC];
+      unpack16(xv[j], f, (const T *)nullptr);
+      unpack16(ld16(g + v * VEC), w, (const T *)nullptr);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) f[e] = f[e] * rinv * w[e];
+      st16(y + v * VEC, pack16(f, (const T *)nullptr));
+    }
   }
 }
 

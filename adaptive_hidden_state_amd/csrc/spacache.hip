@@ -26,6 +26,7 @@ int check_shape(const spa_shape *s, Dims *o) {
   if (s->dtype != SPA_F32 && s->dtype != SPA_BF16) return SPA_ERR_UNSUPPORTED;
   if (s->n_tokens > 16384) return SPA_ERR_UNSUPPORTED;
   if (s->d_model % 64 != 0 || s->d_ffn % 16 != 0) return SPA_ERR_UNSUPPORTED;
+  if (s->d_model > (s->dtype == SPA_BF16 ? 8192 : 4096)) return SPA_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return SPA_ERR_UNSUPPORTED;
   if (s->n_q_heads % s->n_kv_heads != 0) return SPA_ERR_UNSUPPORTED;
   const long long dkv = (long long)s->n_kv_heads * s->head_dim;
@@ -88,8 +89,8 @@ Layout make_layout(const Dims &D, int k_max) {
   L.y = take(m * D.d * D.e);
   L.b1 = take(m * D.d * D.e);
   L.z = take(m * D.F * D.e);
-  // Split-K partials are only used when a GEMM has fewer than 128 tiles; then
-  // splits * M * N < (256 + tiles) * BM * BN <= 384 * 128 * 128.
+  // Split-K partials are only used when a GEMM has fewer than 64 tiles; then
+  // splits * M * N < (256 + tiles) * BM * BN <= 320 * 128 * 128 (bound used below: 384).
   size_t gp = 0;
   const int Ms[1] = {(int)m};
   for (int mm : Ms) {
@@ -112,6 +113,23 @@ Layout make_layout(const Dims &D, int k_max) {
 }
 
 char *at(void *ws, size_t off) { return (char *)ws + off; }
+
+// Optional timing probe: an event recorded on the stream after each kernel (see spa_timing).
+struct Marks {
+  spa_timing *t;
+  hipStream_t s;
+  hipError_t mark(const char *name, int n_kernels = 1) {
+    if (t == nullptr) return hipSuccess;
+    for (int i = 0; i < n_kernels; ++i) {
+      if (t->count >= t->capacity) return hipSuccess;
+      hipError_t e = hipEventRecord(t->marks[t->count], s);
+      if (e != hipSuccess) return e;
+      if (t->names != nullptr && t->count > 0) t->names[t->count - 1] = name;
+      ++t->count;
+    }
+    return hipSuccess;
+  }
+};
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SPA_OK : SPA_ERR_HIP; }
 
@@ -160,18 +178,23 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
 
 // Phase 1 on device: proxy GEMM (fp32 split-K partials) then reduce + cosine + writes.
 int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w_r, const float *pc_read,
-                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s) {
+                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s, Marks &mk) {
   const int rows = D.B * D.N;
   float *part = (float *)at(ws, L.ppart);
   EpiArgs ea{};
   SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, D.d, rows, D.r, D.d, part, ea, s));
+  SPA_TRY(mk.mark("proxy_gemm"));
   SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, s));
+  SPA_TRY(mk.mark("proxy_cosine"));
   return SPA_OK;
 }
 
+// number of kernels launch_gemm enqueues for a plan (the GEMM, plus the split-K reduce)
+int gemm_kernels(const GemmPlan &p) { return p.splits > 1 ? 2 : 1; }
+
 // Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N).
 int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const spa_layer_cache *c,
-               const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s) {
+               const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s, Marks &mk) {
   const int M = D.B * k_per_seq;
   if (M == 0) return SPA_OK;
   void *a1 = at(ws, L.a1), *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *b1 = at(ws, L.b1),
@@ -179,6 +202,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   float *gpart = (float *)at(ws, L.gpart);
 
   SPA_TRY(launch_rmsnorm(D.dtype, h_in, idx, k_per_seq, D.N, M, D.d, w->g_attn, D.eps, a1, s));
+  SPA_TRY(mk.mark("rmsnorm_gather"));
 
   EpiArgs qkv{};
   qkv.out = q;
@@ -192,10 +216,12 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.hkv = D.hkv;
   qkv.hd = D.hd;
   const int nqkv = D.dq + 2 * D.dkv;
-  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV), a1, D.d, w->w_qkv, D.d, M, nqkv,
-                      D.d, gpart, qkv, s));
+  const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);
+  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, a1, D.d, w->w_qkv, D.d, M, nqkv, D.d, gpart, qkv, s));
+  SPA_TRY(mk.mark("qkv_gemm_scatter", gemm_kernels(p_qkv)));
 
   SPA_TRY(launch_attention(D.dtype, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd, s));
+  SPA_TRY(mk.mark("attention"));
 
   EpiArgs wo{};
   wo.out = y;
@@ -205,16 +231,19 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   wo.n_tok = D.N;
   wo.ld_src = D.d;
   wo.ldo = D.d;
-  SPA_TRY(launch_gemm(D.dtype, kEpiResid, plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid), o, D.dq, w->w_o, D.dq, M, D.d,
-                      D.dq, gpart, wo, s));
+  const GemmPlan p_wo = plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid);
+  SPA_TRY(launch_gemm(D.dtype, kEpiResid, p_wo, o, D.dq, w->w_o, D.dq, M, D.d, D.dq, gpart, wo, s));
+  SPA_TRY(mk.mark("wo_gemm_residual", gemm_kernels(p_wo)));
 
   SPA_TRY(launch_rmsnorm(D.dtype, y, nullptr, M, M, M, D.d, w->g_ffn, D.eps, b1, s));
+  SPA_TRY(mk.mark("rmsnorm"));
 
   EpiArgs gu{};
   gu.out = z;
   gu.f = D.F;
-  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, plan_gemm(D.dtype, M, 2 * D.F, D.d, kEpiSwiGLU), b1, D.d, w->w_gate_up,
-                      D.d, M, 2 * D.F, D.d, gpart, gu, s));
+  const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.F, D.d, kEpiSwiGLU);
+  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, b1, D.d, w->w_gate_up, D.d, M, 2 * D.F, D.d, gpart, gu, s));
+  SPA_TRY(mk.mark("gate_up_gemm_swiglu", gemm_kernels(p_gu)));
 
   EpiArgs dn{};
   dn.out = c->h_cache;
@@ -224,8 +253,9 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   dn.n_tok = D.N;
   dn.ld_src = D.d;
   dn.ldo = D.d;
-  SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, plan_gemm(D.dtype, M, D.d, D.F, kEpiResidScatter), z, D.F,
-                      w->w_down, D.F, M, D.d, D.F, gpart, dn, s));
+  const GemmPlan p_dn = plan_gemm(D.dtype, M, D.d, D.F, kEpiResidScatter);
+  SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, p_dn, z, D.F, w->w_down, D.F, M, D.d, D.F, gpart, dn, s));
+  SPA_TRY(mk.mark("down_gemm_scatter", gemm_kernels(p_dn)));
   return SPA_OK;
 }
 
@@ -290,14 +320,19 @@ int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa
   if ((st = check_cache(cache, D, h_in)) != SPA_OK) return st;
   const Layout L = make_layout(D, D.N);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
-  if ((st = run_identify(D, L, h_in, w->w_r, nullptr, cache->p_cache, nullptr, nullptr, ws, stream)) != SPA_OK)
+  Marks mk{nullptr, stream};
+  if ((st = run_identify(D, L, h_in, w->w_r, nullptr, cache->p_cache, nullptr, nullptr, ws, stream, mk)) != SPA_OK)
     return st;
-  return run_sparse(D, L, w, cache, h_in, nullptr, D.N, ws, stream);
+  return run_sparse(D, L, w, cache, h_in, nullptr, D.N, ws, stream, mk);
 }
 
-int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
-                   const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
-                   size_t ws_bytes, hipStream_t stream) {
+int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                         const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
+                         size_t ws_bytes, hipStream_t stream, spa_timing *timing) {
+  if (timing != nullptr) {
+    if (timing->capacity < 0 || (timing->capacity > 0 && timing->marks == nullptr)) return SPA_ERR_INVALID_ARG;
+    timing->count = 0;
+  }
   Dims D;
   int st = check_shape(shape, &D);
   if (st != SPA_OK) return st;
@@ -316,13 +351,25 @@ int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa
   float *scores = scores_out ? scores_out : (float *)at(ws, L.scores);
   const bool sel = policy == SPA_PROXY_WRITE_SELECTED;
   float *pbuf = (float *)at(ws, L.pbuf);
+  Marks mk{timing, stream};
+  SPA_TRY(mk.mark("start"));
   if ((st = run_identify(D, L, h_in, w->w_r, cache->p_cache, sel ? nullptr : cache->p_cache, sel ? pbuf : nullptr,
-                         scores, ws, stream)) != SPA_OK)
+                         scores, ws, stream, mk)) != SPA_OK)
     return st;
   if (k == 0) return SPA_OK;
   SPA_TRY(launch_topk(scores, D.B, D.N, k, idx_out, stream));
-  if (sel) SPA_TRY(launch_copy_selected(pbuf, cache->p_cache, idx_out, D.B, D.N, k, D.r, stream));
-  return run_sparse(D, L, w, cache, h_in, idx_out, k, ws, stream);
+  SPA_TRY(mk.mark("topk"));
+  if (sel) {
+    SPA_TRY(launch_copy_selected(pbuf, cache->p_cache, idx_out, D.B, D.N, k, D.r, stream));
+    SPA_TRY(mk.mark("proxy_copy_selected"));
+  }
+  return run_sparse(D, L, w, cache, h_in, idx_out, k, ws, stream, mk);
+}
+
+int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                   const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  return spa_layer_step_timed(shape, w, cache, h_in, k, policy, idx_out, scores_out, ws, ws_bytes, stream, nullptr);
 }
 
 int spa_identify(const spa_shape *shape, const void *h_in, const void *w_r, const float *p_cache, float *p_out,
@@ -340,7 +387,8 @@ int spa_identify(const spa_shape *shape, const void *h_in, const void *w_r, cons
   if (p_out && p_cache && overlap(p_out, pb, p_cache, pb)) return SPA_ERR_ALIAS;
   const Layout L = make_layout(D, 0);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
-  return run_identify(D, L, h_in, w_r, p_cache, nullptr, p_out, scores_out, ws, stream);
+  Marks mk{nullptr, stream};
+  return run_identify(D, L, h_in, w_r, p_cache, nullptr, p_out, scores_out, ws, stream, mk);
 }
 
 int spa_topk(int32_t batch, int32_t n, const float *scores, int32_t k, int32_t *idx_out, hipStream_t stream) {
@@ -363,7 +411,8 @@ int spa_sparse_update(const spa_shape *shape, const spa_layer_weights *w, const 
   if (idx && !aligned16(idx)) return SPA_ERR_ALIGN;
   const Layout L = make_layout(D, k);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
-  return run_sparse(D, L, w, cache, h_in, idx, k, ws, stream);
+  Marks mk{nullptr, stream};
+  return run_sparse(D, L, w, cache, h_in, idx, k, ws, stream, mk);
 }
 
 int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const void *k_cache, const void *v_cache,

@@ -26,7 +26,8 @@
  *     at the caller's next synchronisation.
  *   - Threads. No global mutable state: concurrent calls on different streams with disjoint
  *     buffers are safe.
- *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0; d_ffn % 16 == 0; head_dim in {64, 128};
+ *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0, d <= 8192 (bf16) or 4096 (fp32);
+ *     d_ffn % 16 == 0; head_dim in {64, 128};
  *     n_q_heads % n_kv_heads == 0; 16 <= r <= 1024, r % 16 == 0, r <= min(d, d_kv).
  */
 #ifndef SPACACHE_H
@@ -120,6 +121,25 @@ int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa
 int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
                    const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Timing probe for profiling tools (not needed for results). The caller creates `capacity` HIP
+ * events; spa_layer_step_timed records marks[0] on the stream before its first kernel and
+ * marks[i + 1] right after its i-th kernel, stopping when capacity is reached, and sets `count` to
+ * the number recorded. names (optional, capacity - 1 entries) receives a static name per kernel:
+ * proxy_gemm, proxy_cosine, topk, [proxy_copy_selected], rmsnorm_gather, qkv_gemm_scatter,
+ * attention, wo_gemm_residual, rmsnorm, gate_up_gemm_swiglu, down_gemm_scatter (a GEMM that splits
+ * K adds a second kernel, its reduce, under the same name). */
+typedef struct {
+  hipEvent_t *marks;
+  int32_t capacity;
+  int32_t count;
+  const char **names;
+} spa_timing;
+
+/* spa_layer_step plus the timing probe above; timing may be NULL. Results are identical. */
+int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                         const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
+                         void *ws, size_t ws_bytes, hipStream_t stream, spa_timing *timing);
 
 /* Phase 1 scores only ([PN] 整体框架 Phase 1; [GS] part 1): p_out = X W_r^T (B x N x r float32) and,
  * when p_cache is not NULL, scores_out = cosine(p, p^c) (B x N). Never writes p_cache.
