@@ -19,8 +19,10 @@ SPA_F32, SPA_BF16 = 0, 1
 SPA_PROXY_WRITE_ALL, SPA_PROXY_WRITE_SELECTED = 0, 1
 
 # Every symbol include/spacache.h declares.
-EXPORTS = ("spa_budget", "spa_workspace_bytes", "spa_layer_full", "spa_layer_step", "spa_layer_step_timed",
-           "spa_identify", "spa_topk", "spa_sparse_update", "spa_attend", "spa_status_string")
+EXPORTS = ("spa_budget", "spa_packed_weight_bytes", "spa_pack_weight", "spa_workspace_bytes", "spa_layer_full",
+           "spa_layer_step", "spa_layer_step_timed", "spa_identify", "spa_topk", "spa_sparse_update", "spa_attend",
+           "spa_status_string")
+SPA_PACK_PLAIN, SPA_PACK_GATE_UP = 0, 1
 
 
 class SpaError(RuntimeError):
@@ -67,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     sig = {
         "spa_budget": ([I32, I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, I32, P, P], ctypes.c_int),
+        "spa_packed_weight_bytes": ([I32, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
+        "spa_pack_weight": ([I32, I32, I32, I32, P, P, P], ctypes.c_int),
         "spa_workspace_bytes": ([P, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "spa_layer_full": ([P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_layer_step": ([P, P, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
@@ -153,7 +157,23 @@ class DeviceCache(NamedTuple):
     p: object  # B x N x r float32
 
 
-def _weights_struct(w: DeviceWeights, tdt) -> spa_layer_weights:
+def _check_bytes(t, need: int, name: str):
+    have = t.numel() * t.element_size()
+    if have < need:
+        raise ValueError(f"{name} holds {have} bytes, needs {need} (weights must be tile-packed: spa_pack_weight)")
+
+
+def _weights_struct(w: DeviceWeights, tdt, shape=None) -> spa_layer_weights:
+    if shape is not None:   # every matrix must be the packed size the kernels will read
+        s = shape
+        dq, dkv = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+        need = {"w_r": (s.rank, s.d_model, SPA_PACK_PLAIN), "w_qkv": (dq + 2 * dkv, s.d_model, SPA_PACK_PLAIN),
+                "w_o": (s.d_model, dq, SPA_PACK_PLAIN), "w_gate_up": (2 * s.d_ffn, s.d_model, SPA_PACK_GATE_UP),
+                "w_down": (s.d_model, s.d_ffn, SPA_PACK_PLAIN)}
+        for f, (r, c, kind) in need.items():
+            _check_bytes(getattr(w, f), spa_packed_weight_bytes(s.dtype, r, c, kind), f)
+        for f in ("g_attn", "g_ffn"):
+            _check_bytes(getattr(w, f), s.d_model * getattr(w, f).element_size(), f)
     return spa_layer_weights(*(_ptr(getattr(w, f), tdt, f) for f in DeviceWeights._fields))
 
 
@@ -199,7 +219,7 @@ def spa_layer_full(shape, w: DeviceWeights, cache: DeviceCache, h_in, ws, stream
     tdt = torch_dtype(shape.dtype)
     s = make_shape(shape)
     wp, wb = _ws(ws)
-    ws_ = _weights_struct(w, tdt)
+    ws_ = _weights_struct(w, tdt, shape)
     cs = _cache_struct(cache, tdt)
     _check(load_library().spa_layer_full(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs), _ptr(h_in, tdt, "h_in"),
                                          wp, wb, _stream(stream)), "spa_layer_full")
@@ -211,7 +231,7 @@ def spa_layer_step(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, po
     tdt = torch_dtype(shape.dtype)
     s = make_shape(shape)
     wp, wb = _ws(ws)
-    ws_ = _weights_struct(w, tdt)
+    ws_ = _weights_struct(w, tdt, shape)
     cs = _cache_struct(cache, tdt)
     _check(load_library().spa_layer_step(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs), _ptr(h_in, tdt, "h_in"),
                                          int(k), int(policy), _ptr(idx_out, torch.int32, "idx_out"),
@@ -258,7 +278,7 @@ def spa_layer_step_timed(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: i
     tdt = torch_dtype(shape.dtype)
     s = make_shape(shape)
     wp, wb = _ws(ws)
-    ws_ = _weights_struct(w, tdt)
+    ws_ = _weights_struct(w, tdt, shape)
     cs = _cache_struct(cache, tdt)
     t = events.timing()
     _check(load_library().spa_layer_step_timed(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs),
@@ -274,6 +294,7 @@ def spa_identify(shape, h_in, w_r, p_cache, p_out, scores_out, ws, stream=None):
     tdt = torch_dtype(shape.dtype)
     s = make_shape(shape)
     wp, wb = _ws(ws)
+    _check_bytes(w_r, spa_packed_weight_bytes(shape.dtype, shape.rank, shape.d_model), "w_r")
     _check(load_library().spa_identify(ctypes.byref(s), _ptr(h_in, tdt, "h_in"), _ptr(w_r, tdt, "w_r"),
                                        _ptr(p_cache, torch.float32, "p_cache"), _ptr(p_out, torch.float32, "p_out"),
                                        _ptr(scores_out, torch.float32, "scores_out"), wp, wb, _stream(stream)),
@@ -295,7 +316,7 @@ def spa_sparse_update(shape, w: DeviceWeights, cache: DeviceCache, h_in, idx, ws
     s = make_shape(shape)
     wp, wb = _ws(ws)
     k = int(idx.shape[-1]) if idx is not None else 0
-    ws_ = _weights_struct(w, tdt)
+    ws_ = _weights_struct(w, tdt, shape)
     cs = _cache_struct(cache, tdt)
     _check(load_library().spa_sparse_update(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs),
                                             _ptr(h_in, tdt, "h_in"), _ptr(idx, torch.int32, "idx"), k, wp, wb,
@@ -313,8 +334,30 @@ def spa_attend(shape, q, m_per_seq: int, k_cache, v_cache, o_out, stream=None):
 # ----------------------------------------------------------------------------------------------
 # device buffers (plumbing: torch allocates, the library computes)
 # ----------------------------------------------------------------------------------------------
+def spa_packed_weight_bytes(dtype, rows: int, cols: int, kind: int = SPA_PACK_PLAIN) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().spa_packed_weight_bytes(dtype_code(dtype), int(rows), int(cols), int(kind),
+                                                  ctypes.byref(out)), "spa_packed_weight_bytes")
+    return int(out.value)
+
+
+def spa_pack_weight(mat, kind: int = SPA_PACK_PLAIN, stream=None):
+    """Tile-packed copy (1-D device tensor) of a row-major device matrix [rows][cols] (y = x W^T)."""
+    import torch
+    if mat.dim() != 2:
+        raise ValueError("weight must be a matrix")
+    dt = "bf16" if mat.dtype == torch.bfloat16 else "f32"
+    rows, cols = mat.shape
+    nbytes = spa_packed_weight_bytes(dt, rows, cols, kind)
+    dst = torch.empty(nbytes // mat.element_size(), dtype=mat.dtype, device=mat.device)
+    _check(load_library().spa_pack_weight(dtype_code(dt), int(rows), int(cols), int(kind), _ptr(mat, None, "weight"),
+                                          _ptr(dst, None, "packed"), _stream(stream)), "spa_pack_weight")
+    return dst
+
+
 def upload_weights(w: dict, w_r, dtype, device="cuda") -> DeviceWeights:
-    """Device weights from host arrays (numpy or torch): concatenates [W_q; W_k; W_v] and [gate; up]."""
+    """Device weights from host arrays (numpy or torch), packed for the GEMMs: [W_q; W_k; W_v],
+    W_o, [W_gate; W_up] (gate/up interleave), W_down and W_r; the gains stay plain vectors."""
     import numpy as np
     import torch
     tdt = torch_dtype(dtype)
@@ -323,9 +366,12 @@ def upload_weights(w: dict, w_r, dtype, device="cuda") -> DeviceWeights:
         t = torch.as_tensor(np.ascontiguousarray(a, dtype=np.float32)) if not isinstance(a, torch.Tensor) else a
         return t.to(device=device, dtype=tdt).contiguous()
 
-    qkv = torch.cat([dev(w["w_q"]), dev(w["w_k"]), dev(w["w_v"])], 0).contiguous()
-    gu = torch.cat([dev(w["w_gate"]), dev(w["w_up"])], 0).contiguous()
-    return DeviceWeights(dev(w_r), qkv, dev(w["w_o"]), gu, dev(w["w_down"]), dev(w["g_attn"]), dev(w["g_ffn"]))
+    qkv = spa_pack_weight(torch.cat([dev(w["w_q"]), dev(w["w_k"]), dev(w["w_v"])], 0).contiguous())
+    gu = spa_pack_weight(torch.cat([dev(w["w_gate"]), dev(w["w_up"])], 0).contiguous(), SPA_PACK_GATE_UP)
+    out = DeviceWeights(spa_pack_weight(dev(w_r)), qkv, spa_pack_weight(dev(w["w_o"])), gu,
+                        spa_pack_weight(dev(w["w_down"])), dev(w["g_attn"]), dev(w["g_ffn"]))
+    torch.cuda.current_stream().synchronize()   # the row-major staging copies are freed after packing
+    return out
 
 
 def alloc_cache(shape, device="cuda") -> DeviceCache:

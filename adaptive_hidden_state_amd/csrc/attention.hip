@@ -184,26 +184,24 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
     }
   };
 
+  // Tiles padded to a multiple of PF keep the loop free of branches around its loads; a padding
+  // tile reads clamped rows and every one of its keys is masked out.
   const int ntiles = (n_tok + KT - 1) / KT;
+  const int ntiles_pad = (ntiles + PF - 1) / PF * PF;
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-    if (u < ntiles) gload(u, rk[u], rv[u]);
+  for (int u = 0; u < PF; ++u) gload(u, rk[u], rv[u]);
   lstore(0, rk[0], rv[0]);
-  if (PF < ntiles) gload(PF, rk[0], rv[0]);
+  gload(PF, rk[0], rv[0]);
   __syncthreads();
-  for (int t0 = 0; t0 < ntiles; t0 += PF) {
+  for (int t0 = 0; t0 < ntiles_pad; t0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int t = t0 + u;
-      if (t < ntiles) {
-        compute(t, t & 1);
-        const int nslot = (u + 1) % PF;
-        if (t + 1 < ntiles) {
-          lstore((t + 1) & 1, rk[nslot], rv[nslot]);
-          if (t + 1 + PF < ntiles) gload(t + 1 + PF, rk[nslot], rv[nslot]);
-        }
-        __syncthreads();
-      }
+      compute(t, t & 1);
+      const int nslot = (u + 1) % PF;
+      lstore((t + 1) & 1, rk[nslot], rv[nslot]);
+      gload(t + 1 + PF, rk[nslot], rv[nslot]);
+      __syncthreads();
     }
   }
 

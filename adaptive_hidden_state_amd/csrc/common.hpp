@@ -75,6 +75,18 @@ __device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 32x32 MFMA blocks. bf16: K = 16 per instruction, 8 values per lane (k = 8*(lane/32) + 0..7).
+// fp32: K = 2 per instruction, 1 value per lane (k = lane/32). A: lane holds row lane%32; B: column
+// lane%32. Output: lane holds column lane%32 and rows 8*(i/4) + 4*(lane/32) + i%4 for i = 0..15.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ floatx16 mfma32(const u32x4 &a, const u32x4 &b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);

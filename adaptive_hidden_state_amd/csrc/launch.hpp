@@ -45,10 +45,26 @@ struct GemmPlan {
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
 
+// A: M x K row-major (lda elements per row). W: tile-packed (see pack.hip), wkb = K blocks per panel.
+// K must be a multiple of the slab width (64 bf16 / 32 fp32 elements).
 // part: workspace for fp32 partials (gemm_partial_bytes), required when plan.splits > 1 or kind is
 // kEpiPartial (then the partials are the result).
 hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W,
-                       int ldw, int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s);
+                       int wkb, int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s);
+
+// Tile-packed weight layout: a row-major R x C matrix becomes blocks of 64 rows x 128 bytes
+// (64 x 64 bf16 or 64 x 32 fp32); rows are padded to a multiple of 128 and columns to a multiple
+// of 64 with zeros; block (i, j) sits at byte offset (i * (C_pad * e / 128) + j) * 8192, row-major
+// inside. kind kPackGateUp reads a [gate; up] source of 2F rows and emits 2 F_pad rows interleaved
+// in groups of 64 (32 gate rows, then the 32 up rows of the same units), F_pad = ceil(F / 64) * 64.
+enum PackKind { kPackPlain = 0, kPackGateUp = 1 };
+inline int pad_to(int v, int m) { return (v + m - 1) / m * m; }
+inline void packed_dims(int kind, int rows, int cols, int *rows_pad, int *cols_pad) {
+  *rows_pad = kind == kPackGateUp ? 2 * pad_to(rows / 2, 64) : pad_to(rows, 128);
+  *cols_pad = pad_to(cols, 64);
+}
+inline int packed_wkb(int dtype, int cols) { return pad_to(cols, 64) * (dtype == kBF16 ? 2 : 4) / 128; }
+hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const void *src, void *dst, hipStream_t s);
 
 // Phase 1 pieces.
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,

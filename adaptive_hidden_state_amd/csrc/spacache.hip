@@ -13,7 +13,7 @@ using namespace spa;
 namespace {
 
 struct Dims {
-  int B, N, d, hq, hkv, hd, F, r, dq, dkv, e, dtype;
+  int B, N, d, hq, hkv, hd, F, Fp, r, dq, dkv, e, dtype;
   float eps;
 };
 
@@ -45,6 +45,7 @@ int check_shape(const spa_shape *s, Dims *o) {
   o->hkv = s->n_kv_heads;
   o->hd = s->head_dim;
   o->F = s->d_ffn;
+  o->Fp = pad_to(s->d_ffn, 64);
   o->r = s->rank;
   o->dq = (int)dq;
   o->dkv = (int)dkv;
@@ -88,15 +89,15 @@ Layout make_layout(const Dims &D, int k_max) {
   L.o = take(m * D.dq * D.e);
   L.y = take(m * D.d * D.e);
   L.b1 = take(m * D.d * D.e);
-  L.z = take(m * D.F * D.e);
-  // Split-K partials are only used when a GEMM has fewer than 64 tiles; then
-  // splits * M * N < (256 + tiles) * BM * BN <= 320 * 128 * 128 (bound used below: 384).
+  L.z = take(m * D.Fp * D.e);
+  // Split-K partials are only used when a GEMM has fewer than 128 tiles; then
+  // splits * M * N <= (256 / tiles + 1) * tiles * BM * BN < 384 * 128 * 128.
   size_t gp = 0;
   const int Ms[1] = {(int)m};
   for (int mm : Ms) {
     if (mm <= 0) continue;
     const int shapes[4][3] = {{D.dq + 2 * D.dkv, D.d, kEpiQKV}, {D.d, D.dq, kEpiResid},
-                              {2 * D.F, D.d, kEpiSwiGLU}, {D.d, D.F, kEpiResidScatter}};
+                              {2 * D.Fp, D.d, kEpiSwiGLU}, {D.d, D.Fp, kEpiResidScatter}};
     for (auto &sh : shapes) {
       const GemmPlan p = plan_gemm(D.dtype, mm, sh[0], sh[1], sh[2]);
       if (p.splits > 1) {
@@ -182,7 +183,8 @@ int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w
   const int rows = D.B * D.N;
   float *part = (float *)at(ws, L.ppart);
   EpiArgs ea{};
-  SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, D.d, rows, D.r, D.d, part, ea, s));
+  SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, packed_wkb(D.dtype, D.d), rows, D.r, D.d, part,
+                      ea, s));
   SPA_TRY(mk.mark("proxy_gemm"));
   SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, s));
   SPA_TRY(mk.mark("proxy_cosine"));
@@ -217,7 +219,8 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.hd = D.hd;
   const int nqkv = D.dq + 2 * D.dkv;
   const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);
-  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, a1, D.d, w->w_qkv, D.d, M, nqkv, D.d, gpart, qkv, s));
+  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, a1, D.d, w->w_qkv, packed_wkb(D.dtype, D.d), M, nqkv, D.d, gpart, qkv,
+                      s));
   SPA_TRY(mk.mark("qkv_gemm_scatter", gemm_kernels(p_qkv)));
 
   SPA_TRY(launch_attention(D.dtype, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd, s));
@@ -232,7 +235,8 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   wo.ld_src = D.d;
   wo.ldo = D.d;
   const GemmPlan p_wo = plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid);
-  SPA_TRY(launch_gemm(D.dtype, kEpiResid, p_wo, o, D.dq, w->w_o, D.dq, M, D.d, D.dq, gpart, wo, s));
+  SPA_TRY(launch_gemm(D.dtype, kEpiResid, p_wo, o, D.dq, w->w_o, packed_wkb(D.dtype, D.dq), M, D.d, D.dq, gpart, wo,
+                      s));
   SPA_TRY(mk.mark("wo_gemm_residual", gemm_kernels(p_wo)));
 
   SPA_TRY(launch_rmsnorm(D.dtype, y, nullptr, M, M, M, D.d, w->g_ffn, D.eps, b1, s));
@@ -240,9 +244,10 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
 
   EpiArgs gu{};
   gu.out = z;
-  gu.f = D.F;
-  const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.F, D.d, kEpiSwiGLU);
-  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, b1, D.d, w->w_gate_up, D.d, M, 2 * D.F, D.d, gpart, gu, s));
+  gu.f = D.Fp;  // Z is M x F_pad; the zero-padded gate/up rows write zeros into the pad columns
+  const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.Fp, D.d, kEpiSwiGLU);
+  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, b1, D.d, w->w_gate_up, packed_wkb(D.dtype, D.d), M, 2 * D.Fp, D.d,
+                      gpart, gu, s));
   SPA_TRY(mk.mark("gate_up_gemm_swiglu", gemm_kernels(p_gu)));
 
   EpiArgs dn{};
@@ -253,8 +258,9 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   dn.n_tok = D.N;
   dn.ld_src = D.d;
   dn.ldo = D.d;
-  const GemmPlan p_dn = plan_gemm(D.dtype, M, D.d, D.F, kEpiResidScatter);
-  SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, p_dn, z, D.F, w->w_down, D.F, M, D.d, D.F, gpart, dn, s));
+  const GemmPlan p_dn = plan_gemm(D.dtype, M, D.d, D.Fp, kEpiResidScatter);
+  SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, p_dn, z, D.Fp, w->w_down, packed_wkb(D.dtype, D.F), M, D.d, D.Fp,
+                      gpart, dn, s));
   SPA_TRY(mk.mark("down_gemm_scatter", gemm_kernels(p_dn)));
   return SPA_OK;
 }
@@ -300,6 +306,29 @@ int spa_budget(int32_t n_layers, int32_t l_peak, double rho_peak, double rho_fir
     if (k_out != nullptr) k_out[l - 1] = (int32_t)kk;
   }
   return SPA_OK;
+}
+
+int spa_packed_weight_bytes(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, size_t *bytes_out) {
+  if (dtype != SPA_F32 && dtype != SPA_BF16) return SPA_ERR_UNSUPPORTED;
+  if (kind != SPA_PACK_PLAIN && kind != SPA_PACK_GATE_UP) return SPA_ERR_INVALID_ARG;
+  if (rows < 1 || cols < 1 || bytes_out == nullptr) return SPA_ERR_INVALID_ARG;
+  if (kind == SPA_PACK_GATE_UP && rows % 2 != 0) return SPA_ERR_INVALID_ARG;
+  if (cols % 16 != 0 || (kind == SPA_PACK_GATE_UP && (rows / 2) % 16 != 0)) return SPA_ERR_UNSUPPORTED;
+  int rp, cp;
+  packed_dims(kind, rows, cols, &rp, &cp);
+  *bytes_out = (size_t)rp * cp * (dtype == SPA_BF16 ? 2 : 4);
+  return SPA_OK;
+}
+
+int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src, void *dst,
+                    hipStream_t stream) {
+  size_t bytes = 0;
+  const int st = spa_packed_weight_bytes(dtype, rows, cols, kind, &bytes);
+  if (st != SPA_OK) return st;
+  if (src == nullptr || dst == nullptr) return SPA_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return SPA_ERR_ALIGN;
+  if (overlap(src, (size_t)rows * cols * (dtype == SPA_BF16 ? 2 : 4), dst, bytes)) return SPA_ERR_ALIAS;
+  return hip_status(launch_pack_weight(dtype, kind, rows, cols, src, dst, stream));
 }
 
 int spa_workspace_bytes(const spa_shape *shape, int32_t k_max, size_t *bytes_out) {

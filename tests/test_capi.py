@@ -202,3 +202,18 @@ def test_offline_proxy_matches_oracle():
     assert np.allclose(c.T @ c, svd.T @ svd, rtol=0, atol=1e-5 * np.abs(svd.T @ svd).max())
     with pytest.raises(ValueError):
         offline.singular_proxy_from_factors(ww["v_lambda"], ww["v_right"], 4, g_attn=np.full(64, 2.0))
+
+
+def test_packed_weight_bytes(lib):
+    from adaptive_hidden_state_amd import binding
+    assert binding.spa_packed_weight_bytes("bf16", 12288, 4096) == 12288 * 4096 * 2
+    assert binding.spa_packed_weight_bytes("bf16", 100, 80) == 128 * 128 * 2          # rows to 128, cols to 64
+    assert binding.spa_packed_weight_bytes("f32", 16, 256) == 128 * 256 * 4
+    assert binding.spa_packed_weight_bytes("bf16", 2 * 688, 256, 1) == 2 * 704 * 256 * 2   # gate/up: 2 F_pad rows
+    out = ctypes.c_size_t(0)
+    assert lib.spa_packed_weight_bytes(1, 100, 81, 0, ctypes.byref(out)) == -2          # cols % 16
+    assert lib.spa_packed_weight_bytes(1, 101, 80, 1, ctypes.byref(out)) == -1          # odd gate/up rows
+    assert lib.spa_packed_weight_bytes(5, 100, 80, 0, ctypes.byref(out)) == -2          # dtype
+    assert lib.spa_packed_weight_bytes(1, 100, 80, 3, ctypes.byref(out)) == -1          # kind
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x1000 + 64), None) == -3
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1008), _fake(0x100000), None) == -4

@@ -212,7 +212,8 @@ def test_identify_scores_and_proxy(shape):
     p_out = torch.empty(s.batch, s.n_tokens, s.rank, dtype=torch.float32, device="cuda")
     scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
     pc = torch.from_numpy(case.cache0.p.astype(np.float32)).cuda()
-    spa.spa_identify(s, dev(case.x1, s.dtype), dev(case.w_r, s.dtype), pc, p_out, scores, spa.alloc_workspace(s, 0))
+    w_r = spa.spa_pack_weight(dev(case.w_r, s.dtype))
+    spa.spa_identify(s, dev(case.x1, s.dtype), w_r, pc, p_out, scores, spa.alloc_workspace(s, 0))
     torch.cuda.synchronize()
     p_o, s_o = oracle.identify(case.x1, case.w_r, case.cache0.p)
     assert np.max(np.abs(host(scores) - s_o)) <= 1e-3
@@ -302,3 +303,42 @@ def test_dream_layer_step_full_size():
     pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
     case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
     _check_step(case, int(ks[9]))          # layer 10 = the peak: k = 512
+
+
+def _pack_reference(w, kind, e):
+    """The tile-packed layout written out on the host: 64-row x 128-byte blocks, zero padding,
+    gate/up rows interleaved in groups of 64 (32 gate rows, then the 32 up rows of the same units)."""
+    rows, cols = w.shape
+    bke = 128 // e
+    cols_pad = -(-cols // 64) * 64
+    if kind == 1:
+        f = rows // 2
+        fp = -(-f // 64) * 64
+        logical = np.zeros((2 * fp, cols), w.dtype)
+        for r in range(2 * fp):
+            q, ww = divmod(r, 64)
+            j = q * 32 + (ww % 32)
+            if j < f:
+                logical[r] = w[j] if ww < 32 else w[f + j]
+        rows_pad = 2 * fp
+    else:
+        rows_pad = -(-rows // 128) * 128
+        logical = np.zeros((rows_pad, cols), w.dtype)
+        logical[:rows] = w
+    full = np.zeros((rows_pad, cols_pad), w.dtype)
+    full[:, :cols] = logical
+    blocks = full.reshape(rows_pad // 64, 64, cols_pad // bke, bke).transpose(0, 2, 1, 3)
+    return blocks.reshape(-1)
+
+
+@pytest.mark.parametrize("dtype,rows,cols,kind", [("bf16", 200, 96, 0), ("bf16", 2 * 688, 256, 1),
+                                                  ("f32", 16, 256, 0), ("f32", 2 * 48, 80, 1)])
+def test_pack_weight_layout_bit_exact(dtype, rows, cols, kind):
+    import torch
+    spa = _lib()
+    rng = np.random.default_rng(rows + cols)
+    w = synth.to_storage(rng.standard_normal((rows, cols)), dtype)
+    packed = spa.spa_pack_weight(dev(w, dtype), kind)
+    torch.cuda.synchronize()
+    ref = _pack_reference(w.astype(np.float32), kind, 2 if dtype == "bf16" else 4)
+    assert np.array_equal(packed.float().cpu().numpy(), ref)
