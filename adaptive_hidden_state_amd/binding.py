@@ -242,14 +242,18 @@ def spa_layer_step(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, po
 class HipEvents:
     """`n` HIP timing events (created through the HIP runtime) for spa_layer_step_timed."""
 
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
     def __init__(self, n: int):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.n = n
         self.events = (ctypes.c_void_p * n)()
         for i in range(n):
             ev = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            # no system-scope fence when an event completes: the marks sit between kernels of one
+            # stream and are only read back on the host after a synchronize
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.events[i] = ev
         self.names = (ctypes.c_char_p * max(n - 1, 1))()
 

@@ -16,6 +16,7 @@ baseline on the host cores.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -52,6 +53,86 @@ def gemm_work(name, s, M):
     return byts, flops
 
 
+KERNEL_SOURCES = {
+    "gemm": ("adaptive_hidden_state_amd/csrc/gemm.hip", "adaptive_hidden_state_amd/csrc/common.hpp",
+             "adaptive_hidden_state_amd/csrc/launch.hpp"),
+}
+
+
+def kernel_source_hash(family):
+    """sha256 over the sources that define a kernel family (to tell whether counters are current)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary of this kernel and workload, or None
+    when there is none or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    try:
+        if fields["source_sha256"] != kernel_source_hash(fields["family"]):
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_profile(trace_csv=None, counter_csvs=()):
+    """Text summary of rocprofv3 CSV output: per (kernel, grid) dispatch count and average/median
+    duration from a --kernel-trace run, and per (kernel, grid) average counter values from --pmc runs."""
+    import csv
+    import statistics
+
+    def short(name):
+        name = re.sub(r"^void ", "", name)
+        name = re.sub(r"\(.*$", "", name)
+        return name.replace("unsigned short", "bf16").replace("spa::", "")
+
+    def grid_of(row):
+        if "Grid_Size" in row:
+            return int(row["Grid_Size"]), int(row["Workgroup_Size"])
+        g = int(row["Grid_Size_X"]) * int(row["Grid_Size_Y"]) * int(row["Grid_Size_Z"])
+        wg = int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"])
+        return g, wg
+
+    out = []
+    if trace_csv:
+        groups = {}
+        with open(trace_csv) as f:
+            for row in csv.DictReader(f):
+                g, wg = grid_of(row)
+                dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+                groups.setdefault((short(row["Kernel_Name"]), g // wg, wg), []).append(dur)
+        out.append(f"{'kernel':64s} {'workgroups':>10s} {'wg':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s}")
+        for (name, nwg, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{name[:64]:64s} {nwg:10d} {wg:5d} {len(v):6d} {sum(v) / len(v):9.2f} "
+                       f"{statistics.median(v):9.2f}")
+    for path in counter_csvs:
+        groups = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                g, wg = grid_of(row)
+                groups.setdefault((short(row["Kernel_Name"]), g // wg, wg, row["Counter_Name"]), []).append(
+                    float(row["Counter_Value"]))
+        out.append("")
+        out.append(f"{'kernel':64s} {'workgroups':>10s} {'wg':>5s} {'counter':>12s} {'calls':>6s} {'avg':>14s}")
+        for (name, nwg, wg, cn), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{name[:64]:64s} {nwg:10d} {wg:5d} {cn:>12s} {len(v):6d} {sum(v) / len(v):14.1f}")
+    return "\n".join(out)
+
+
 def cpu_baseline(wl, w, w_r, xs, k, seconds):
     """The oracle's cached layer step timed on the host cores (bounded sample)."""
     import numpy as np
@@ -86,7 +167,13 @@ def main():
     ap.add_argument("--workload", default="llada-layer", choices=["llada-layer", "tiny-f32"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV", nargs="*", default=[],
+                    help="summarise rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_counters:
+        print(summarize_profile(args.summarize_trace, args.summarize_counters))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -182,7 +269,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": flops / dur_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom, wl.name)
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = byts
     roof["algorithmic_flops"] = flops
