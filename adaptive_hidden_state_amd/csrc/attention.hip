@@ -1,13 +1,20 @@
 // Partial cached attention ([PN] 整体框架 Phase 2): the k queries of the update set attend,
 // bidirectionally and without a mask, to all N keys of the (already scattered) K^c/V^c cache.
 //
-// One workgroup = one (sequence, query head, block of 32 * QW queries); each wave owns 32 queries.
-// Keys stream through LDS in tiles of 64: K as [key][hd] and V transposed to [hd][key], so that both
-// products read contiguous LDS. A wave computes S^T = K Q^T (keys x queries) on 32x32 MFMA blocks;
-// in that layout a lane holds 32 scores of one query, so the online softmax (fp32, base-2 exponent)
-// needs one cross-lane step, and the probabilities feed O^T = V^T P^T straight from registers.
-// V is transposed on the way into LDS: each thread loads an 8-key x 8-dim block (eight 16-byte row
-// pieces), transposes it in registers and writes eight 16-byte rows of V^T.
+// One workgroup = one (sequence, query head, block of 32 queries) and four waves. The keys are split
+// into four contiguous ranges, one per wave; each wave runs an online softmax over its range and the
+// four partial results (running max, running sum, unnormalised output) are merged through LDS at the
+// end. Every wave streams its own key tiles (64 keys) through a private LDS region: K as [key][hd] and
+// V transposed to [hd][key], so that both products read contiguous LDS; no barrier is needed inside
+// the key loop (a wave's LDS accesses complete in order). A wave computes S^T = K Q^T (keys x queries)
+// on 32x32 MFMA blocks; in that layout a lane holds the scores of one query, so the softmax (fp32,
+// base-2 exponent) needs one cross-lane step, and the probabilities feed O^T = V^T P^T straight from
+// registers. V is transposed on the way into LDS: a lane loads an 8-key x 8-dim block (eight 16-byte
+// row pieces), transposes it in registers and writes eight 16-byte rows of V^T.
+//
+// Workgroup ids are remapped so that each XCD (which receives every eighth workgroup) runs a
+// contiguous range of (sequence, KV head, query head, query block): the blocks that read the same K/V
+// head share that XCD's L2, and HBM sees each head's K/V about once.
 // Query head h reads KV head h / (H_q / H_kv) (grouped-query attention).
 #include "common.hpp"
 #include "launch.hpp"
@@ -30,38 +37,62 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 *in, u32x4 *out) {
   }
 }
 
-template <typename T, int HD, int QW>
-__global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict__ q, const T *__restrict__ kc,
-                                                            const T *__restrict__ vc, T *__restrict__ o,
-                                                            int m_per_seq, int n_tok, int hq, int hkv,
-                                                            float scale_log2) {
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int NT = 64 * QW;
-  constexpr int KT = 64;                                  // keys per tile
-  constexpr int KROWB = HD * (int)sizeof(T) + 16;         // K tile row stride (bytes)
-  constexpr int VROWB = KT * (int)sizeof(T) + 16;         // V^T tile row stride (bytes)
+constexpr int kAttnWaves = 4;     // key ranges per workgroup
+constexpr int kAttnQueries = 32;  // queries per workgroup
+
+template <typename T, int HD> struct AttnCfg {
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int KT = (BF || HD == 64) ? 64 : 32;            // keys per tile
+  static constexpr int KROWB = HD * (int)sizeof(T) + 16;           // K tile row stride (bytes)
+  static constexpr int VROWB = KT * (int)sizeof(T) + 16;           // V^T tile row stride (bytes)
+  static constexpr int WAVE_BYTES = KT * KROWB + HD * VROWB;       // private LDS of one wave
+  static constexpr int PROWB = (HD + 4) * 4;                       // merge buffer row (fp32 O of a query)
+  static_assert(kAttnQueries * PROWB + kAttnQueries * 8 <= WAVE_BYTES, "merge buffer fits a wave region");
+  static_assert(kAttnWaves * WAVE_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
+    const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc, T *__restrict__ o,
+    int m_per_seq, int n_tok, int hq, int hkv, int qblocks, int nwg, float scale_log2) {
+  typedef AttnCfg<T, HD> C;
+  constexpr bool BF = C::BF;
+  constexpr int KT = C::KT;
+  constexpr int NKB = KT / 32;                            // 32-key MFMA blocks per tile
+  constexpr int KROWB = C::KROWB, VROWB = C::VROWB;
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int KCH = KT * HD / VEC / NT;                 // K 16-byte chunks per thread per tile
+  constexpr int KCH = KT * HD / VEC / 64;                 // K 16-byte chunks per lane per tile
   // V: bf16 uses 8x8 blocks (8 key rows x one 16-byte chunk); fp32 uses 4x4 blocks
   constexpr int VB = BF ? 8 : 4;
   constexpr int VTASKS = (KT / VB) * (HD / VB);           // blocks per tile
-  constexpr int VPER = (VTASKS + NT - 1) / NT;
+  constexpr int VPER = VTASKS / 64;
   constexpr int QSTEPS = BF ? HD / 16 : HD / 2;           // MFMA k-steps over the head dim
   constexpr int KSTEP_B = BF ? 32 : 8;
   constexpr int LANE_B = BF ? 16 : 4;
   constexpr int HB = HD / 32;                             // 32-row blocks of the head dim
-  constexpr int PF = 2;                                   // key tiles in flight in registers
-  static_assert(KT * HD % (VEC * NT) == 0, "K tile load split");
+  static_assert(KT * HD % (VEC * 64) == 0 && VTASKS % 64 == 0, "tile load split");
   typedef typename AFrag<BF>::type FragT;
 
-  __shared__ __attribute__((aligned(16))) char ks[2][KT * KROWB];
-  __shared__ __attribute__((aligned(16))) char vts[2][HD * VROWB];
+  __shared__ __attribute__((aligned(16))) char smem[kAttnWaves * C::WAVE_BYTES];
+
+  // XCD-aware order: hardware hands workgroup i to XCD i % 8
+  const int nb = gridDim.x;
+  const int lid = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+  if (lid >= nwg) return;  // grid padding (whole workgroup, before any barrier)
+  const int grp = hq / hkv;
+  const int qb = lid % qblocks;
+  int rest = lid / qblocks;
+  const int h_in = rest % grp;
+  rest /= grp;
+  const int g = rest % hkv;
+  const int b = rest / hkv;
+  const int h = g * grp + h_in;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int g = h / (hq / hkv);
-  const int m0 = blockIdx.x * (32 * QW) + wave * 32;
+  const int m0 = qb * kAttnQueries;
   const int ldq = hq * HD;
+  char *ks = smem + wave * C::WAVE_BYTES;
+  char *vts = ks + KT * KROWB;
 
   // Q fragments: B operand of S^T = K Q^T (column = query lane%32, k = head dim).
   FragT qf[QSTEPS];
@@ -88,77 +119,95 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
+  // This wave's tiles: [t_begin, t_begin + nt).
+  const int ntiles = (n_tok + KT - 1) / KT;
+  const int tper = (ntiles + kAttnWaves - 1) / kAttnWaves;
+  const int t_begin = wave * tper;
+  const int nt = max(0, min(tper, ntiles - t_begin));
+
   // V block assignment: block id v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so
   // the lanes that write one V^T row segment hold consecutive key blocks (conflict-free LDS).
-  u32x4 rk[PF][KCH], rv[PF][VPER][VB];
-  auto gload = [&](int t, u32x4 *xk, u32x4 (*xv)[VB]) {
+  u32x4 rk[KCH], rv[VPER][VB];
+  auto gload = [&](int t) {  // rows past the end are clamped to the last key (masked later)
     const int key0 = t * KT;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * NT;
+      const int c = lane + j * 64;
       const int row = c / (HD / VEC), col = c % (HD / VEC);
       const int key = min(key0 + row, n_tok - 1);
-      xk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
+      rk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
     }
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
-      const int v = min(tid + p * NT, VTASKS - 1);
+      const int v = lane + p * 64;
       const int kb = v % (KT / VB), cc = v / (KT / VB);
 #pragma unroll
       for (int j = 0; j < VB; ++j) {
         const int key = min(key0 + kb * VB + j, n_tok - 1);
-        xv[p][j] = ld16(vbase + (size_t)key * HD + cc * VB);
+        rv[p][j] = ld16(vbase + (size_t)key * HD + cc * VB);
       }
     }
   };
-  auto lstore = [&](int buf, const u32x4 *xk, u32x4 (*xv)[VB]) {
+  auto lstore = [&]() {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * NT;
+      const int c = lane + j * 64;
       const int row = c / (HD / VEC), col = c % (HD / VEC);
-      st16(ks[buf] + row * KROWB + col * 16, xk[j]);
+      st16(ks + row * KROWB + col * 16, rk[j]);
     }
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
-      const int v = tid + p * NT;
-      if (v < VTASKS) {
-        const int kb = v % (KT / VB), cc = v / (KT / VB);
-        if constexpr (BF) {
-          u32x4 tr[8];
-          transpose8x8_b16(xv[p], tr);
+      const int v = lane + p * 64;
+      const int kb = v % (KT / VB), cc = v / (KT / VB);
+      if constexpr (BF) {
+        u32x4 tr[8];
+        transpose8x8_b16(rv[p], tr);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) st16(vts[buf] + (cc * 8 + e) * VROWB + kb * 16, tr[e]);
-        } else {
+        for (int e = 0; e < 8; ++e) st16(vts + (cc * 8 + e) * VROWB + kb * 16, tr[e]);
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const u32x4 col = {xv[p][0][e], xv[p][1][e], xv[p][2][e], xv[p][3][e]};
-            st16(vts[buf] + (cc * 4 + e) * VROWB + kb * 16, col);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const u32x4 col = {rv[p][0][e], rv[p][1][e], rv[p][2][e], rv[p][3][e]};
+          st16(vts + (cc * 4 + e) * VROWB + kb * 16, col);
         }
       }
     }
   };
 
-  auto compute = [&](int t, int buf) {
-    // S^T blocks (64 keys = 2 blocks of 32): lane holds query lane%32 and keys
+  auto compute = [&](int t) {
+    // S^T blocks of 32 keys: lane holds query lane%32 and keys
     // kb*32 + 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15
-    floatx16 s[2], s2[2];
+    floatx16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = s2[kb][r] = 0.f;
-      const char *krow = ks[buf] + (kb * 32 + (lane & 31)) * KROWB + (lane >> 5) * LANE_B;
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    if constexpr (NKB == 2) {
+      // two independent MFMA chains: the two key blocks
+      const char *krow0 = ks + (lane & 31) * KROWB + (lane >> 5) * LANE_B;
+      const char *krow1 = krow0 + 32 * KROWB;
+#pragma unroll
+      for (int st = 0; st < QSTEPS; ++st) {
+        s[0] = mfma32(*reinterpret_cast<const FragT *>(krow0 + st * KSTEP_B), qf[st], s[0]);
+        s[1] = mfma32(*reinterpret_cast<const FragT *>(krow1 + st * KSTEP_B), qf[st], s[1]);
+      }
+    } else {
+      // one key block: two chains over the even and odd head-dim steps
+      floatx16 s2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[r] = 0.f;
+      const char *krow = ks + (lane & 31) * KROWB + (lane >> 5) * LANE_B;
 #pragma unroll
       for (int st = 0; st < QSTEPS; st += 2) {
-        s[kb] = mfma32(*reinterpret_cast<const FragT *>(krow + st * KSTEP_B), qf[st], s[kb]);
-        s2[kb] = mfma32(*reinterpret_cast<const FragT *>(krow + (st + 1) * KSTEP_B), qf[st + 1], s2[kb]);
+        s[0] = mfma32(*reinterpret_cast<const FragT *>(krow + st * KSTEP_B), qf[st], s[0]);
+        s2 = mfma32(*reinterpret_cast<const FragT *>(krow + (st + 1) * KSTEP_B), qf[st + 1], s2);
       }
-      s[kb] += s2[kb];
+      s[0] += s2;
     }
     // raw scores; the softmax scale (and log2 e) is applied inside one FMA per score
     if (t * KT + KT > n_tok) {  // partial last tile (uniform branch): mask keys past the end
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * KT + kb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -167,14 +216,14 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
-    const float mnew = fmaxf(mrun, tmax);
+    const float mnew = fmaxf(mrun, tmax);  // finite: a wave's first tile holds at least one key
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2f(fmaf(s[kb][r], scale_log2, -mnew));
@@ -195,7 +244,7 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
     // half*8+7, i.e. keys kb*32 + half*16 + {4G..4G+3, 8+4G..8+4G+3}; A = V^T rows at those keys.
     const int G = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if constexpr (BF) {
@@ -207,7 +256,7 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
           const int c0 = (kb * 32 + half * 16 + 4 * G) * 2, c1 = c0 + 16;
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
-            const char *vrow = vts[buf] + (hb * 32 + (lane & 31)) * VROWB;
+            const char *vrow = vts + (hb * 32 + (lane & 31)) * VROWB;
             const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
             const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
             const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
@@ -221,7 +270,7 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
             const int key = kb * 32 + (r >> 2) * 8 + G * 4 + (r & 3);
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
-              const float vf = *reinterpret_cast<const float *>(vts[buf] + (hb * 32 + (lane & 31)) * VROWB + key * 4);
+              const float vf = *reinterpret_cast<const float *>(vts + (hb * 32 + (lane & 31)) * VROWB + key * 4);
               oacc[hb] = mfma32(vf, s[kb][r], oacc[hb]);
             }
           }
@@ -229,49 +278,86 @@ __global__ __launch_bounds__(64 * QW) void attention_kernel(const T *__restrict_
       }
   };
 
-  // Tiles padded to a multiple of PF keep the loop free of branches around its loads; a padding
-  // tile reads clamped rows and every one of its keys is masked out.
-  const int ntiles = (n_tok + KT - 1) / KT;
-  const int ntiles_pad = (ntiles + PF - 1) / PF * PF;
-#pragma unroll
-  for (int u = 0; u < PF; ++u) gload(u, rk[u], rv[u]);
-  lstore(0, rk[0], rv[0]);
-  gload(PF, rk[0], rv[0]);
-  __syncthreads();
-  for (int t0 = 0; t0 < ntiles_pad; t0 += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int t = t0 + u;
-      compute(t, u & 1);
-      const int nslot = (u + 1) % PF;
-      lstore((u + 1) & 1, rk[nslot], rv[nslot]);
-      gload(t + 1 + PF, rk[nslot], rv[nslot]);
-      __syncthreads();
+  // One tile in registers ahead of the one in LDS. Branches depend only on the wave's tile count.
+  if (nt > 0) {
+    gload(t_begin);
+    lstore();
+    gload(t_begin + 1);
+    for (int i = 0; i < nt; ++i) {
+      compute(t_begin + i);
+      if (i + 1 < nt) {
+        lstore();
+        gload(t_begin + i + 2);
+      }
     }
   }
 
+  // Merge the four key ranges. Each wave parks its partial state in its own LDS region (whose K/V
+  // tiles only it reads), then all threads combine.
   lrun += __shfl_xor(lrun, 32, kWave);
-  const float inv = 1.0f / lrun;
-  const int qo = m0 + (lane & 31);
-  if (qo < m_per_seq) {
-    // lane holds O^T[hd = hb*32 + 8*(r/4) + 4*(lane/32) + r%4][query]: 4 consecutive dims per r/4
-    T *op = o + ((size_t)b * m_per_seq + qo) * ldq + (size_t)h * HD + (lane >> 5) * 4;
+  {
+    char *part = ks;
+    const int G = lane >> 5;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float v0 = oacc[hb][r4 * 4 + 0] * inv, v1 = oacc[hb][r4 * 4 + 1] * inv;
-        const float v2 = oacc[hb][r4 * 4 + 2] * inv, v3 = oacc[hb][r4 * 4 + 3] * inv;
-        T *dst = op + hb * 32 + r4 * 8;
-        if constexpr (BF) {
-          u32x2 w;
-          w[0] = pack_bf16x2(v0, v1);
-          w[1] = pack_bf16x2(v2, v3);
-          *reinterpret_cast<u32x2 *>(dst) = w;
-        } else {
-          *reinterpret_cast<floatx4 *>(dst) = floatx4{v0, v1, v2, v3};
-        }
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<floatx4 *>(part + (lane & 31) * C::PROWB + (hb * 32 + r4 * 8 + G * 4) * 4) =
+            floatx4{oacc[hb][r4 * 4 + 0], oacc[hb][r4 * 4 + 1], oacc[hb][r4 * 4 + 2], oacc[hb][r4 * 4 + 3]};
+    if (lane < 32) {
+      float *ml = reinterpret_cast<float *>(part + kAttnQueries * C::PROWB);
+      ml[2 * lane] = mrun;
+      ml[2 * lane + 1] = lrun;
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int SEG = HD / 8;  // dims per thread: 8 threads per query
+    const int qi = tid >> 3, d0 = (tid & 7) * SEG;
+    float mw[kAttnWaves], lw[kAttnWaves];
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float *ml = reinterpret_cast<const float *>(smem + w * C::WAVE_BYTES + kAttnQueries * C::PROWB);
+      mw[w] = ml[2 * qi];
+      lw[w] = ml[2 * qi + 1];
+      mmax = fmaxf(mmax, mw[w]);
+    }
+    float aw[kAttnWaves], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      aw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - mmax);  // a wave without keys adds nothing
+      lsum = fmaf(aw[w], lw[w], lsum);
+    }
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) aw[w] *= inv;
+    float acc[SEG];
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const char *row = smem + w * C::WAVE_BYTES + qi * C::PROWB + d0 * 4;
+#pragma unroll
+      for (int e = 0; e < SEG; e += 4) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(row + e * 4);
+        acc[e] = fmaf(aw[w], v[0], acc[e]);
+        acc[e + 1] = fmaf(aw[w], v[1], acc[e + 1]);
+        acc[e + 2] = fmaf(aw[w], v[2], acc[e + 2]);
+        acc[e + 3] = fmaf(aw[w], v[3], acc[e + 3]);
       }
+    }
+    const int qo = m0 + qi;
+    if (qo < m_per_seq) {
+      T *dst = o + ((size_t)b * m_per_seq + qo) * ldq + (size_t)h * HD + d0;
+#pragma unroll
+      for (int e = 0; e < SEG; e += VEC) {
+        if constexpr (BF)
+          st16(dst + e, pack16(acc + e, (const bf16_t *)nullptr));
+        else
+          st16(dst + e, pack16(acc + e, (const float *)nullptr));
+      }
+    }
   }
 }
 
@@ -279,9 +365,13 @@ template <typename T, int HD>
 static hipError_t run_attention(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
                                 int n_tok, int hq, int hkv, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  dim3 grid((m_per_seq + 63) / 64, hq, batch);
-  hipLaunchKernelGGL((attention_kernel<T, HD, 2>), grid, dim3(128), 0, s, (const T *)q, (const T *)kc,
-                     (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, scale_log2);
+  const int qblocks = (m_per_seq + kAttnQueries - 1) / kAttnQueries;
+  const long long nwg = (long long)qblocks * hq * batch;
+  if (nwg > (1LL << 30)) return hipErrorInvalidValue;
+  const int grid = (int)((nwg + 7) / 8 * 8);
+  hipLaunchKernelGGL((attention_kernel<T, HD>), dim3(grid), dim3(64 * kAttnWaves), 0, s, (const T *)q,
+                     (const T *)kc, (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, qblocks, (int)nwg,
+                     scale_log2);
   return hipGetLastError();
 }
 
