@@ -2,99 +2,129 @@
 // ([PN] 整体框架 phases 2 and 3: Q/K/V of the update set with the K/V cache scatter, W_o with the
 // residual, the SwiGLU gate/up product, and W_down with the residual scattered into H^c).
 //
-// A (M x K) and W (rows x K) are both K-contiguous, which is the operand order the 16x16 MFMA wants:
-// every lane reads 16 contiguous bytes of a row for each k-step. Tiles are staged through LDS in
-// 128-byte K slabs (64 bf16 / 32 fp32), double-buffered, with a 16-byte row pad so that the 16 rows a
-// quarter-wave reads land on distinct LDS banks. Workgroups of one XCD get a contiguous range of
-// tiles, M fastest, so tiles that share a weight panel run together behind the same L2.
+// Weights are fragment-packed (pack.hip): every (32-row block, 16-k step) of W is one contiguous
+// kilobyte laid out in the lane order of the 32x32 MFMA B operand, so a wave loads its B fragments
+// straight from memory into registers with one fully coalesced 16-byte load per lane; weights never
+// pass through LDS. Only the activation tile A (BM rows x 128-byte K slabs) is staged through LDS,
+// double-buffered, rows padded to 144 bytes so the 32 rows a fragment read touches sit on distinct
+// banks.
+//
+// A workgroup has four waves: two column halves (wn) x two K halves (wk). Wave (wn, wk) owns all BM
+// rows and BN/2 columns and runs the MFMA k-steps of its K half of every slab, so no weight fragment
+// is loaded twice in a workgroup and each A fragment read from LDS feeds BN/64 MFMAs. The two K
+// halves are added through LDS at the end; each wave then finishes half of the rows.
+// Workgroups of one XCD get a contiguous range of tiles, M fastest, so the M tiles that share a
+// weight panel run together behind the same L2.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace spa {
 
-// The gate/up weight is packed with its rows interleaved in groups of 64 (32 gate rows j..j+31, then
-// the 32 up rows with the same j), so one lane of a pair of 32x32 MFMA blocks holds gate and up of
-// the same unit: output column n holds hidden unit (n / 64) * 32 + n % 32, gate when n % 64 < 32.
+// The gate/up weight is packed so that each 32-row block holds the gate rows of 16 hidden units
+// followed by the up rows of the same 16 units: output column n is unit (n / 32) * 16 + n % 16, gate
+// when n % 32 < 16, and lanes l and l ^ 16 of a 32x32 MFMA block hold gate and up of one unit.
 
 __device__ __forceinline__ int map_token(const EpiArgs &ea, int m, int &b) {
   b = m / ea.k_per_seq;
   return ea.idx ? ea.idx[m] : (m - b * ea.k_per_seq);
 }
 
+// Eight consecutive elements of T <-> floats (one 16-byte access for bf16, two for fp32).
+__device__ __forceinline__ void load8(const bf16_t *p, float *v) { unpack16(ld16(p), v, p); }
+__device__ __forceinline__ void load8(const float *p, float *v) {
+  unpack16(ld16(p), v, p);
+  unpack16(ld16(p + 4), v + 4, p);
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float *v) { st16(p, pack16(v, p)); }
+__device__ __forceinline__ void store8(float *p, const float *v) {
+  st16(p, pack16(v, p));
+  st16(p + 4, pack16(v + 4, p));
+}
+
+// Epilogue of output row m, columns n0 .. n0 + 7 (n0 % 8 == 0; every width here is a multiple of 8,
+// and so is every head or hidden-unit boundary, so the eight never straddle one).
 template <typename T, int KIND>
-__device__ __forceinline__ void epi_store(const EpiArgs &ea, int m, int n, float v) {
+__device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const float *v) {
   if constexpr (KIND == kEpiQKV) {
-    if (n < ea.dq) {
-      ((T *)ea.out)[(size_t)m * ea.dq + n] = from_f32<T>(v);
+    if (n0 < ea.dq) {
+      store8((T *)ea.out + (size_t)m * ea.dq + n0, v);
       return;
     }
     int b;
     const int i = map_token(ea, m, b);
     if ((unsigned)i >= (unsigned)ea.n_tok) return;
-    int nn = n - ea.dq;
+    int nn = n0 - ea.dq;
     T *dst = (T *)ea.out2;
     if (nn >= ea.dkv) {
       nn -= ea.dkv;
       dst = (T *)ea.out3;
     }
     const int g = nn / ea.hd, e = nn - g * ea.hd;
-    dst[(((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e] = from_f32<T>(v);
+    store8(dst + (((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e, v);
   } else if constexpr (KIND == kEpiResid) {
     int b;
     int i = map_token(ea, m, b);
     i = min(max(i, 0), ea.n_tok - 1);
-    const float r = to_f32<T>(((const T *)ea.src)[((size_t)b * ea.n_tok + i) * ea.ld_src + n]);
-    ((T *)ea.out)[(size_t)m * ea.ldo + n] = from_f32<T>(r + v);
+    float r[8];
+    load8((const T *)ea.src + ((size_t)b * ea.n_tok + i) * ea.ld_src + n0, r);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) r[x] += v[x];
+    store8((T *)ea.out + (size_t)m * ea.ldo + n0, r);
   } else if constexpr (KIND == kEpiResidScatter) {
     int b;
     const int i = map_token(ea, m, b);
     if ((unsigned)i >= (unsigned)ea.n_tok) return;
-    const float r = to_f32<T>(((const T *)ea.src)[(size_t)m * ea.ld_src + n]);
-    ((T *)ea.out)[((size_t)b * ea.n_tok + i) * ea.ldo + n] = from_f32<T>(r + v);
+    float r[8];
+    load8((const T *)ea.src + (size_t)m * ea.ld_src + n0, r);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) r[x] += v[x];
+    store8((T *)ea.out + ((size_t)b * ea.n_tok + i) * ea.ldo + n0, r);
   } else if constexpr (KIND == kEpiPartial) {
-    ((float *)ea.out)[(size_t)m * ea.ldo + n] = v;
+    store8((float *)ea.out + (size_t)m * ea.ldo + n0, v);
   }
 }
 
+// z[m][j0 .. j0 + 7] = silu(gate) * up
 template <typename T>
-__device__ __forceinline__ void epi_swiglu(const EpiArgs &ea, int m, int j, float g, float u) {
-  const float s = g / (1.0f + __expf(-g));
-  ((T *)ea.out)[(size_t)m * ea.f + j] = from_f32<T>(s * u);
+__device__ __forceinline__ void epi8_swiglu(const EpiArgs &ea, int m, int j0, const float *g, const float *u) {
+  float z[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) z[x] = g[x] / (1.0f + __expf(-g[x])) * u[x];
+  store8((T *)ea.out + (size_t)m * ea.f + j0, z);
 }
 
-template <bool BF16> struct Frag;
-template <> struct Frag<true> { typedef u32x4 type; };
-template <> struct Frag<false> { typedef float type; };
+template <int BM, int BN> struct GemmLds {
+  static constexpr int kA = 2 * BM * 144;                        // double-buffered A slabs
+  static constexpr int kRed = 2 * (BM / 32) * (BN / 64) * 4096;  // one K half's blocks, both column halves
+  static constexpr int kStride = BN / 2 + 4;                     // staged output row (floats)
+  static constexpr int kEpi = 4 * (BM / 2) * kStride * 4;        // each wave's BM/2 x BN/2 fp32 rows
+  static constexpr int kBytes = kA > kRed ? (kA > kEpi ? kA : kEpi) : (kRed > kEpi ? kRed : kEpi);
+};
 
-// C[m][n] = sum_k A[m][k] W[n][k] on 32x32 MFMA blocks. A is row-major (lda elements per row). W is
-// tile-packed: blocks of 64 rows x 128 bytes, block (i, j) at byte offset (i * wkb + j) * 8192, so
-// the K slab of one 64-row panel is a contiguous 8 KB run and a workgroup streams its weight panel
-// sequentially. K (and every split) is a multiple of the slab width; rows past N are zero.
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int KIND, int PF>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
-    const T *__restrict__ A, int lda, const T *__restrict__ W, int wkb, int M, int N, int K, int tiles_m,
-    int tiles_n, int k_split, float *__restrict__ part, EpiArgs ea) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int BK = 128 / sizeof(T);
+// C[m][n] = sum_k A[m][k] W[n][k]. A is row-major (lda elements per row). W is fragment-packed with
+// wkb blocks per 32-row block. K (and every split) is a multiple of the 128-byte slab; columns past
+// N are computed from clamped blocks and never stored.
+template <typename T, int BM, int BN, int KIND, int PF>
+__global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int lda, const char *__restrict__ W,
+                                                   int wkb, int M, int N, int K, int tiles_m, int tiles_n,
+                                                   int k_split, float *__restrict__ part, EpiArgs ea) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int BK = 128 / (int)sizeof(T);   // K elements per slab
+  constexpr int BKF = BF ? 16 : 8;           // K elements per packed block
   constexpr int ROWB = 144;
-  constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_PER = BM * 8 / NT, B_PER = BN * 8 / NT;
-  constexpr bool IS_BF16 = sizeof(T) == 2;
-  constexpr int KSTEP_B = IS_BF16 ? 32 : 8;   // bytes of one row per MFMA k-step
-  constexpr int LANE_B = IS_BF16 ? 16 : 4;    // bytes per lane per k-step
-  constexpr int KSTEPS = 128 / KSTEP_B;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile loads must divide evenly");
-  static_assert(BN % 64 == 0, "weight panels are 64 rows");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 blocks");
-  static_assert(KIND != kEpiSwiGLU || (WTN % 64 == 0), "gate/up pairs must stay inside a wave");
+  constexpr int FM = BM / 32, FN = BN / 64;  // 32x32 blocks of a wave tile (BM x BN/2)
+  constexpr int A_PER = BM * 8 / 256;        // 16-byte A chunks per thread per slab
+  constexpr int KSTEP_B = BF ? 32 : 8;       // bytes of an A row per MFMA k-step
+  constexpr int LANE_B = BF ? 16 : 4;        // bytes per lane per k-step
+  constexpr int KPB = BF ? 1 : 4;            // MFMA k-steps per packed block
+  static_assert(FM % 2 == 0 && FN >= 1 && BM * 8 % 256 == 0, "tile shape");
   static_assert(PF == 2 || PF == 4, "prefetch depth must be even");
-  typedef typename Frag<IS_BF16>::type FragT;
+  typedef GemmLds<BM, BN> L;
 
-  __shared__ __attribute__((aligned(16))) char lds[2][(BM + BN) * ROWB];
+  __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int wn = wave & 1, wk = wave >> 1;
 
   int bid = blockIdx.x;
   const int nb = gridDim.x;
@@ -108,46 +138,49 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   const int nk = k1 > k0 ? (k1 - k0) / BK : 0;
 
   const char *a_src[A_PER];
-  const char *b_src[B_PER];
-  int a_dst[A_PER], b_dst[B_PER];
+  int a_dst[A_PER];
 #pragma unroll
   for (int j = 0; j < A_PER; ++j) {
-    const int c = tid + j * NT, row = c >> 3, col = c & 7;
+    const int c = tid + j * 256, row = c >> 3, col = c & 7;
     const int gr = min(tm * BM + row, M - 1);
     a_src[j] = reinterpret_cast<const char *>(A + (size_t)gr * lda + k0) + col * 16;
     a_dst[j] = row * ROWB + col * 16;
   }
+  // B: this wave's column blocks, blocks 2 wk and 2 wk + 1 of every slab (four blocks per slab)
+  const int cb0 = (tn * BN + wn * (BN / 2)) / 32;
+  const int cb_last = (N + 31) / 32 - 1;
+  const char *b_src[FN];
 #pragma unroll
-  for (int j = 0; j < B_PER; ++j) {
-    const int c = tid + j * NT, row = c >> 3, col = c & 7;
-    const int panel = tn * (BN / 64) + (row >> 6);
-    b_src[j] = reinterpret_cast<const char *>(W) + (((size_t)panel * wkb + k0 / BK) * 64 + (row & 63)) * 128 + col * 16;
-    b_dst[j] = BM * ROWB + row * ROWB + col * 16;
+  for (int j = 0; j < FN; ++j) {
+    const int cb = min(cb0 + j, cb_last);
+    b_src[j] = W + ((size_t)cb * wkb + k0 / BKF + 2 * wk) * 1024 + lane * 16;
   }
 
-  // Register ring of PF K slabs in flight: slab kt lives in slot kt % PF from its load until it is
-  // written to LDS one iteration before it is used. Loads are unconditional (the slab index is
-  // clamped), so the compiler waits for exactly the oldest slab; the slab count is padded to a
-  // multiple of PF and padding slabs enter LDS with A zeroed, contributing nothing.
-  u32x4 ra[PF][A_PER], rb[PF][B_PER];
+  // Register ring of PF K slabs in flight: slab kt lives in slot kt % PF from its load until its A part
+  // is written to LDS (one iteration before use) and its B fragments are consumed. Loads are
+  // unconditional (the slab index is clamped), so the compiler waits for exactly the oldest slab; the
+  // slab count is padded to a multiple of PF and padding slabs enter LDS with A zeroed.
+  u32x4 ra[PF][A_PER], rb[PF][2 * FN];
   const u32x4 zero = {0u, 0u, 0u, 0u};
   auto gload = [&](int kt, u32x4 *xa, u32x4 *xb) {
     const int kc = min(kt, nk - 1);
 #pragma unroll
     for (int j = 0; j < A_PER; ++j) xa[j] = ld16(a_src[j] + (size_t)kc * 128);
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j) xb[j] = ld16(b_src[j] + (size_t)kc * 8192);
+    for (int j = 0; j < FN; ++j) {
+      xb[2 * j] = ld16(b_src[j] + (size_t)kc * 4096);
+      xb[2 * j + 1] = ld16(b_src[j] + (size_t)kc * 4096 + 1024);
+    }
   };
-  auto lstore = [&](int buf, int kt, const u32x4 *xa, const u32x4 *xb) {
+  auto lstore = [&](int buf, int kt, const u32x4 *xa) {
+    char *dst = lds + buf * BM * ROWB;
     if (kt < nk) {
 #pragma unroll
-      for (int j = 0; j < A_PER; ++j) st16(&lds[buf][a_dst[j]], xa[j]);
+      for (int j = 0; j < A_PER; ++j) st16(dst + a_dst[j], xa[j]);
     } else {
 #pragma unroll
-      for (int j = 0; j < A_PER; ++j) st16(&lds[buf][a_dst[j]], zero);
+      for (int j = 0; j < A_PER; ++j) st16(dst + a_dst[j], zero);
     }
-#pragma unroll
-    for (int j = 0; j < B_PER; ++j) st16(&lds[buf][b_dst[j]], xb[j]);
   };
 
   floatx16 acc[FM][FN];
@@ -162,8 +195,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
   if (nk > 0) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) gload(u, ra[u], rb[u]);
-    lstore(0, 0, ra[0], rb[0]);
-    gload(PF, ra[0], rb[0]);
+    lstore(0, 0, ra[0]);
   }
   __syncthreads();
 
@@ -172,90 +204,149 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int kt = kt0 + u;
-      const int cur = u & 1;  // PF is even, so slab kt0 + u sits in LDS buffer u & 1
-      const char *As = &lds[cur][(wm * WTM) * ROWB + frag_off];
-      const char *Bs = &lds[cur][BM * ROWB + (wn * WTN) * ROWB + frag_off];
+      const char *As = lds + (u & 1) * BM * ROWB + frag_off;  // PF is even: slab kt0 + u is in buffer u & 1
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        FragT af[FM], bfr[FN];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const FragT *>(As + i * 32 * ROWB + ks * KSTEP_B);
+        for (int s = 0; s < KPB; ++s) {
+          const int ks = (2 * wk + t) * KPB + s;  // k-step within the slab
+          if constexpr (BF) {
+            u32x4 af[FM];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const FragT *>(Bs + j * 32 * ROWB + ks * KSTEP_B);
+            for (int i = 0; i < FM; ++i) af[i] = ld16(As + i * 32 * ROWB + ks * KSTEP_B);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-      }
+              for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], rb[u][2 * j + t], acc[i][j]);
+          } else {
+            float af[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const float *>(As + i * 32 * ROWB + ks * KSTEP_B);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], __uint_as_float(rb[u][2 * j + t][s]), acc[i][j]);
+          }
+        }
       const int nslot = (u + 1) % PF;
-      lstore(cur ^ 1, kt + 1, ra[nslot], rb[nslot]);
-      gload(kt + 1 + PF, ra[nslot], rb[nslot]);
+      lstore((u + 1) & 1, kt + 1, ra[nslot]);
+      gload(kt + PF, ra[u], rb[u]);
       __syncthreads();
     }
   }
 
-  // lane holds column lane % 32 and rows 8 * (q / 4) + 4 * (lane / 32) + q % 4 of each 32x32 block
-  const int row0 = tm * BM + wm * WTM + (lane >> 5) * 4;
-  const int col0 = tn * BN + wn * WTN + (lane & 31);
+  // Add the two K halves: wave (wn, wk) keeps row blocks [wk FM/2, (wk+1) FM/2) and hands the others
+  // to its partner (wn, 1 - wk) through LDS (16-byte chunks, lane-contiguous: conflict-free).
+  constexpr int HM = FM / 2;
+  auto red_at = [&](int i, int j, int c) { return lds + (((wn * FM + i) * FN + j) * 4 + c) * 1024 + lane * 16; };
+  floatx16 own[HM][FN];
+#pragma unroll
+  for (int hi = 0; hi < HM; ++hi)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const floatx16 give = wk ? acc[hi][j] : acc[HM + hi][j];
+      own[hi][j] = wk ? acc[HM + hi][j] : acc[hi][j];
+      const int gi = wk ? hi : HM + hi;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        st16(red_at(gi, j, c), u32x4{__float_as_uint(give[4 * c]), __float_as_uint(give[4 * c + 1]),
+                                     __float_as_uint(give[4 * c + 2]), __float_as_uint(give[4 * c + 3])});
+    }
+  __syncthreads();
+#pragma unroll
+  for (int hi = 0; hi < HM; ++hi)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int oi = wk ? HM + hi : hi;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = ld16(red_at(oi, j, c));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) own[hi][j][4 * c + x] += __uint_as_float(v[x]);
+      }
+    }
+  __syncthreads();
+
+  // Stage this wave's BM/2 x BN/2 result row-major in its own LDS region, then let every lane finish
+  // eight consecutive columns of a row at a time (one 16-byte store for bf16; per-row indexing once).
+  // A lane holds column lane % 32 and rows 8 (q / 4) + 4 (lane / 32) + q % 4 of each 32x32 block.
+  constexpr int ER = HM * 32, EC = FN * 32, ES = L::kStride;
+  float *ep = reinterpret_cast<float *>(lds) + wave * ER * ES;
+#pragma unroll
+  for (int hi = 0; hi < HM; ++hi)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        ep[(hi * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3)) * ES + j * 32 + (lane & 31)] = own[hi][j][q];
+  // the wave reads back only what it wrote (in-order LDS within a wave)
+  const int mbase = tm * BM + wk * ER;
+  const int nbase = tn * BN + wn * EC;
   if (part != nullptr) {
-    float *P = part + (size_t)split * M * N;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = row0 + i * 32 + (q >> 2) * 8 + (q & 3), n = col0 + j * 32;
-          if (m < M && n < N) P[(size_t)m * N + n] = acc[i][j][q];
-        }
+    EpiArgs pe{};
+    pe.out = part + (size_t)split * M * N;
+    pe.ldo = N;
+    for (int idx = lane; idx < ER * EC / 8; idx += 64) {
+      const int lr = idx / (EC / 8), c8 = idx - lr * (EC / 8);
+      const int m = mbase + lr, n0 = nbase + c8 * 8;
+      if (m < M && n0 < N) epi8<T, kEpiPartial>(pe, m, n0, ep + lr * ES + c8 * 8);
+    }
     return;
   }
   if constexpr (KIND == kEpiSwiGLU) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; j += 2)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = row0 + i * 32 + (q >> 2) * 8 + (q & 3), n = col0 + j * 32;
-          if (m < M && n < N) epi_swiglu<T>(ea, m, (n >> 6) * 32 + (n & 63), acc[i][j][q], acc[i][j + 1][q]);
-        }
+    // columns 32 c + 0..15 are the gate rows of units 16 c + 0..15, columns 32 c + 16..31 their up rows
+    for (int idx = lane; idx < ER * EC / 16; idx += 64) {
+      const int lr = idx / (EC / 16), g8 = idx - lr * (EC / 16);
+      const int c = g8 >> 1, h = g8 & 1;
+      const int m = mbase + lr, j0 = (nbase / 32 + c) * 16 + h * 8;
+      const float *row = ep + lr * ES + c * 32 + h * 8;
+      if (m < M && j0 < ea.f) epi8_swiglu<T>(ea, m, j0, row, row + 16);
+    }
   } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int m = row0 + i * 32 + (q >> 2) * 8 + (q & 3), n = col0 + j * 32;
-          if (m < M && n < N) epi_store<T, KIND>(ea, m, n, acc[i][j][q]);
-        }
+    for (int idx = lane; idx < ER * EC / 8; idx += 64) {
+      const int lr = idx / (EC / 8), c8 = idx - lr * (EC / 8);
+      const int m = mbase + lr, n0 = nbase + c8 * 8;
+      if (m < M && n0 < N) epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
+    }
   }
 }
 
-// Sum of the split-K partials in split order (deterministic), then the epilogue.
+// Sum of the split-K partials in split order (deterministic), then the epilogue, eight columns (or
+// eight hidden units) per thread.
 template <typename T, int KIND>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits, int M,
                                                             int N, EpiArgs ea) {
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t plane = (size_t)M * N;
   if constexpr (KIND == kEpiSwiGLU) {
-    const int f = ea.f;
-    if (t >= (size_t)M * f) return;
-    const int m = (int)(t / f), j = (int)(t - (size_t)m * f);
-    const int ng = (j >> 5) * 64 + (j & 31);
-    float g = 0.f, u = 0.f;
+    const int f8 = ea.f / 8;
+    if (t >= (size_t)M * f8) return;
+    const int m = (int)(t / f8), j0 = (int)(t - (size_t)m * f8) * 8;
+    const int ng = (j0 >> 4) * 32 + (j0 & 15);
+    float g[8] = {}, u[8] = {};
     for (int s = 0; s < splits; ++s) {
-      g += part[s * plane + (size_t)m * N + ng];
-      u += part[s * plane + (size_t)m * N + ng + 32];
+      float a[8], c[8];
+      load8(part + s * plane + (size_t)m * N + ng, a);
+      load8(part + s * plane + (size_t)m * N + ng + 16, c);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        g[x] += a[x];
+        u[x] += c[x];
+      }
     }
-    epi_swiglu<T>(ea, m, j, g, u);
+    epi8_swiglu<T>(ea, m, j0, g, u);
   } else {
-    if (t >= plane) return;
-    const int m = (int)(t / N), n = (int)(t - (size_t)m * N);
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[s * plane + t];
-    epi_store<T, KIND>(ea, m, n, v);
+    const int n8 = N / 8;
+    if (t >= (size_t)M * n8) return;
+    const int m = (int)(t / n8), n0 = (int)(t - (size_t)m * n8) * 8;
+    float v[8] = {};
+    for (int s = 0; s < splits; ++s) {
+      float a[8];
+      load8(part + s * plane + (size_t)m * N + n0, a);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) v[x] += a[x];
+    }
+    epi8<T, KIND>(ea, m, n0, v);
   }
 }
 
@@ -263,78 +354,81 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // host side: tile plans and dispatch
 // ---------------------------------------------------------------------------------------------
 namespace {
-constexpr int kTargetWGs = 256;  // one workgroup per CU of an MI355X
+constexpr int kCUs = 256;
 
 struct TileCfg {
   int bm, bn;
 };
-// 0: fp32 128x64 (4x1 waves of 32x64); 1: bf16 128x128 (2x2 waves of 64x64); 2: bf16 64x128 (2x2 waves
-// of 32x64); 3: bf16 128x64 (2x2 waves of 64x32, not for the gate/up pairs)
-constexpr TileCfg kTiles[4] = {{128, 64}, {128, 128}, {64, 128}, {128, 64}};
+// bf16 tiles 0..5; fp32 uses tile 5 only
+constexpr TileCfg kTiles[6] = {{128, 192}, {64, 192}, {128, 128}, {128, 64}, {64, 128}, {64, 64}};
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
+
+// Cost model of one launch in CU clocks, fitted to MI355X measurements of these kernels: a workgroup
+// costs its K range times the larger of its load time (weight panel from HBM, A tile mostly from L2)
+// and its MFMA time; workgroups run one per CU in rounds; split-K adds the fp32 partial round trip
+// and a second launch.
+double plan_cost(int bm, int bn, int M, int N, int K, int splits, int kc) {
+  const long long tiles = (long long)ceil_div(M, bm) * ceil_div(N, bn);
+  const long long wgs = tiles * splits;
+  const double rounds = (double)ceil_div_ll(wgs, kCUs);
+  const double load = (bn + 0.5 * bm) / 14.0;
+  const double mfma = (double)bm * bn / 1638.0;
+  double t = rounds * kc * (load > mfma ? load : mfma);
+  if (splits > 1) t += (double)M * N * splits * 8.0 / (kCUs * 28.0) + 4000.0;
+  return t;
+}
 }  // namespace
 
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
-  // Measured on MI355X for the k-row GEMMs (M = 256): 128x128 tiles without split-K whenever they
-  // give at least half a workgroup per CU; otherwise split K so the grid reaches one workgroup per CU,
-  // on 128x128 tiles when each split keeps >= 2048 of K, else on 128x64 tiles.
-  GemmPlan p{};
+  GemmPlan best{};
   const int bk = dtype == kF32 ? 32 : 64;
-  int splits = 1;
-  if (dtype == kF32) {
-    p.cfg = 0;
-  } else if (M <= 64) {
-    p.cfg = 2;
-    const int t2 = ceil_div(N, 128);
-    if (kind != kEpiPartial && t2 < kTargetWGs / 2) splits = ceil_div(kTargetWGs, t2);
-  } else {
-    p.cfg = 1;
-    const int t1 = ceil_div(M, 128) * ceil_div(N, 128);
-    if (kind != kEpiPartial && t1 < kTargetWGs / 2) {
-      splits = ceil_div(kTargetWGs, t1);
-      if (K / splits < 2048 && kind != kEpiSwiGLU) {
-        p.cfg = 3;
-        splits = ceil_div(kTargetWGs, ceil_div(M, 128) * ceil_div(N, 64));
+  double best_cost = 0.0;
+  const int ncfg = dtype == kF32 ? 1 : 6;
+  for (int ci = 0; ci < ncfg; ++ci) {
+    const int cfg = dtype == kF32 ? 5 : ci;
+    const TileCfg tc = kTiles[cfg];
+    for (int s = 1; s <= 16; ++s) {
+      int kc = ceil_div(ceil_div(K, s), bk) * bk;
+      const int splits = ceil_div(K, kc);
+      if (splits != s) continue;                  // duplicate of a smaller split count
+      if (splits > 1 && kc < 4 * bk) break;       // keep at least four slabs per split
+      if (splits > 1 && (long long)ceil_div(M, tc.bm) * ceil_div(N, tc.bn) * splits > kMaxSplitWGs) break;
+      double cost = plan_cost(tc.bm, tc.bn, M, N, K, splits, kc);
+      if (kind == kEpiPartial) cost -= (splits > 1) ? 4000.0 : 0.0;  // partials are the output anyway
+      if (best.bm == 0 || cost < best_cost) {
+        best_cost = cost;
+        best.cfg = cfg;
+        best.bm = tc.bm;
+        best.bn = tc.bn;
+        best.splits = splits;
+        best.k_split = kc;
       }
     }
   }
-  p.bm = kTiles[p.cfg].bm;
-  p.bn = kTiles[p.cfg].bn;
-  p.tiles_m = ceil_div(M, p.bm);
-  p.tiles_n = ceil_div(N, p.bn);
-  const int tiles = p.tiles_m * p.tiles_n;
-  if (kind == kEpiPartial) splits = ceil_div(kTargetWGs, tiles);
-  int max_splits = K / (bk * 4) > 1 ? K / (bk * 4) : 1;
-  if (max_splits > 16) max_splits = 16;
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int ks = ceil_div(K, splits);
-  ks = ceil_div(ks, bk) * bk;
-  p.k_split = ks;
-  p.splits = ceil_div(K, ks);
-  return p;
+  best.tiles_m = ceil_div(M, best.bm);
+  best.tiles_n = ceil_div(N, best.bn);
+  return best;
 }
 
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N) {
   return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
-template <typename T, int BM, int BN, int WMv, int WNv, int KIND>
+template <typename T, int BM, int BN, int KIND>
 static hipError_t run_gemm(const GemmPlan &p, const void *A, int lda, const void *W, int wkb, int M, int N,
                            int K, float *part, const EpiArgs &ea, hipStream_t s) {
   constexpr int PF = 4;
   const bool use_part = (KIND == kEpiPartial) || p.splits > 1;
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
-  EpiArgs e = ea;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WMv, WNv, KIND, PF>), dim3(grid), dim3(64 * WMv * WNv), 0, s,
-                     (const T *)A, lda, (const T *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, p.k_split,
-                     use_part ? part : nullptr, e);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, KIND, PF>), dim3(grid), dim3(256), 0, s, (const T *)A, lda,
+                     (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, p.k_split, use_part ? part : nullptr, ea);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || KIND == kEpiPartial || p.splits == 1) return err;
-  const size_t work = KIND == kEpiSwiGLU ? (size_t)M * ea.f : (size_t)M * N;
+  const size_t work = (KIND == kEpiSwiGLU ? (size_t)M * ea.f : (size_t)M * N) / 8;
   const unsigned rgrid = (unsigned)((work + 255) / 256);
-  hipLaunchKernelGGL((splitk_reduce_kernel<T, KIND>), dim3(rgrid), dim3(256), 0, s, part, p.splits, M, N, e);
+  hipLaunchKernelGGL((splitk_reduce_kernel<T, KIND>), dim3(rgrid), dim3(256), 0, s, part, p.splits, M, N, ea);
   return hipGetLastError();
 }
 
@@ -342,14 +436,15 @@ template <typename T, int KIND>
 static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void *W, int wkb, int M, int N, int K,
                           float *part, const EpiArgs &ea, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
-    return run_gemm<T, 128, 64, 4, 1, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+    return run_gemm<T, 64, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
   } else {
     switch (p.cfg) {
-      case 1: return run_gemm<T, 128, 128, 2, 2, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
-      case 3:
-        if constexpr (KIND != kEpiSwiGLU) return run_gemm<T, 128, 64, 2, 2, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
-        return hipErrorInvalidValue;
-      default: return run_gemm<T, 64, 128, 2, 2, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case 0: return run_gemm<T, 128, 192, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case 1: return run_gemm<T, 64, 192, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case 2: return run_gemm<T, 128, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case 3: return run_gemm<T, 128, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case 4: return run_gemm<T, 64, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      default: return run_gemm<T, 64, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
     }
   }
 }

@@ -45,25 +45,36 @@ struct GemmPlan {
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
 
-// A: M x K row-major (lda elements per row). W: tile-packed (see pack.hip), wkb = K blocks per panel.
-// K must be a multiple of the slab width (64 bf16 / 32 fp32 elements).
+// A: M x K row-major (lda elements per row). W: fragment-packed (see below), wkb = packed blocks per
+// 32-row block. K must be a multiple of the slab width (64 bf16 / 32 fp32 elements).
 // part: workspace for fp32 partials (gemm_partial_bytes), required when plan.splits > 1 or kind is
 // kEpiPartial (then the partials are the result).
 hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W,
                        int wkb, int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s);
 
-// Tile-packed weight layout: a row-major R x C matrix becomes blocks of 64 rows x 128 bytes
-// (64 x 64 bf16 or 64 x 32 fp32); rows are padded to a multiple of 128 and columns to a multiple
-// of 64 with zeros; block (i, j) sits at byte offset (i * (C_pad * e / 128) + j) * 8192, row-major
-// inside. kind kPackGateUp reads a [gate; up] source of 2F rows and emits 2 F_pad rows interleaved
-// in groups of 64 (32 gate rows, then the 32 up rows of the same units), F_pad = ceil(F / 64) * 64.
+// Split-K plans keep splits * tiles <= kMaxSplitWGs, so their partials never exceed
+// kMaxSplitWGs * 128 * 192 fp32 values, nor 16 * M * N.
+constexpr int kMaxSplitWGs = 512;
+inline size_t gemm_partial_bound(int M, int N) {
+  const size_t a = (size_t)16 * M * N * 4, b = (size_t)kMaxSplitWGs * 128 * 192 * 4;
+  return a < b ? a : b;
+}
+
+// Fragment-packed weight layout: a row-major R x C matrix becomes 1 KB blocks, one per (32-row block
+// rb, K block kb) with 16 bf16 or 8 fp32 K elements per block, at byte offset (rb * wkb + kb) * 1024,
+// wkb = C_pad / (16 or 8). Inside a block, lane l = 0..63 of a wave owns the 16 bytes at l * 16: the
+// B operand of a 32x32 MFMA for output column l % 32 -- bf16: k = 16 kb + 8 (l / 32) + j, j = 0..7;
+// fp32: k = 8 kb + 2 j + l / 32, j = 0..3 (four 32x32x2 k-steps). Rows are padded to a multiple of
+// 32 and columns to a multiple of 64 with zeros. kind kPackGateUp reads a [gate; up] source of 2F
+// rows and packs 2 F_pad rows (F_pad = ceil(F / 64) * 64) where 32-row block rb holds the gate rows
+// of units 16 rb .. 16 rb + 15 followed by the up rows of the same units.
 enum PackKind { kPackPlain = 0, kPackGateUp = 1 };
 inline int pad_to(int v, int m) { return (v + m - 1) / m * m; }
 inline void packed_dims(int kind, int rows, int cols, int *rows_pad, int *cols_pad) {
-  *rows_pad = kind == kPackGateUp ? 2 * pad_to(rows / 2, 64) : pad_to(rows, 128);
+  *rows_pad = kind == kPackGateUp ? 2 * pad_to(rows / 2, 64) : pad_to(rows, 32);
   *cols_pad = pad_to(cols, 64);
 }
-inline int packed_wkb(int dtype, int cols) { return pad_to(cols, 64) * (dtype == kBF16 ? 2 : 4) / 128; }
+inline int packed_wkb(int dtype, int cols) { return pad_to(cols, 64) / (dtype == kBF16 ? 16 : 8); }
 hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const void *src, void *dst, hipStream_t s);
 
 // Phase 1 pieces.

@@ -1,8 +1,9 @@
-// Tile-packed weight layout. A GEMM workgroup reads its weight panel one K slab (64 rows x 128 bytes)
-// at a time; in a row-major matrix those 64 rows are 128-byte pieces scattered C * e bytes apart,
-// which HBM serves at a small fraction of its bandwidth. Packing each 64 x 128-byte block into one
-// contiguous 8 KB run turns every workgroup's panel into a sequential stream. The padding (rows to
-// 128, columns to 64, zero-filled) also removes every K-tail and N-tail case from the GEMM.
+// Fragment-packed weight layout (the layout is defined next to packed_dims in launch.hpp). A GEMM
+// wave consumes its weights as 32x32 MFMA B fragments: for every (32-row block, 16-k step) each lane
+// holds 16 bytes of one row. Storing each such fragment as one contiguous kilobyte in lane order
+// lets the wave fetch it with a single fully coalesced 16-byte load per lane, straight into the
+// registers the MFMA reads, and lets every weight panel stream from HBM as long sequential runs. The
+// zero padding (rows to 32, columns to 64) removes the K-tail and N-tail cases from the GEMM.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -12,27 +13,38 @@ template <typename T>
 __global__ __launch_bounds__(256) void pack_weight_kernel(const T *__restrict__ src, int rows, int cols,
                                                           int rows_pad, int cols_pad, int gate_up_f,
                                                           T *__restrict__ dst) {
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int BKE = 128 / (int)sizeof(T);
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int BKF = BF ? 16 : 8;  // K elements per block
   const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte chunk of dst
-  const size_t nchunks = (size_t)rows_pad * cols_pad / VEC;
+  const size_t nchunks = (size_t)rows_pad * cols_pad * sizeof(T) / 16;
   if (t >= nchunks) return;
-  const int kb = cols_pad / BKE;
-  const size_t blk = t / 512;
-  const int within = (int)(t % 512);
-  const int bi = (int)(blk / kb), bj = (int)(blk % kb);
-  const int r = bi * 64 + within / 8;
-  const int c0 = bj * BKE + (within % 8) * VEC;
+  const int wkb = cols_pad / BKF;
+  const size_t blk = t >> 6;
+  const int l = (int)(t & 63);
+  const int rb = (int)(blk / wkb), kb = (int)(blk % wkb);
+  const int w = l & 31;
+  const int r = rb * 32 + w;
   int sr = r;
-  bool valid = r < rows && c0 < cols;
-  if (gate_up_f > 0) {  // logical row r = 64 q + w: gate (w < 32) or up row of unit 32 q + w % 32
-    const int q = r >> 6, w = r & 63;
-    const int j = q * 32 + (w & 31);
-    valid = j < gate_up_f && c0 < cols;
-    sr = (w < 32) ? j : gate_up_f + j;
+  bool valid = r < rows;
+  if (gate_up_f > 0) {  // block rb: gate rows of units 16 rb .. 16 rb + 15, then their up rows
+    const int u = rb * 16 + (w & 15);
+    valid = u < gate_up_f;
+    sr = (w < 16) ? u : gate_up_f + u;
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  st16(dst + t * VEC, valid ? ld16(src + (size_t)sr * cols + c0) : zero);
+  if constexpr (BF) {
+    const int c0 = kb * BKF + (l >> 5) * 8;  // 8 consecutive K elements (cols is a multiple of 16)
+    st16(dst + t * 8, (valid && c0 < cols) ? ld16(src + (size_t)sr * cols + c0) : zero);
+  } else {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = kb * BKF + 2 * j + (l >> 5);
+      v[j] = (valid && c < cols) ? src[(size_t)sr * cols + c] : 0.f;
+    }
+    st16(dst + t * 4, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                            __float_as_uint(v[3])});
+  }
 }
 
 hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const void *src, void *dst, hipStream_t s) {

@@ -90,24 +90,16 @@ Layout make_layout(const Dims &D, int k_max) {
   L.y = take(m * D.d * D.e);
   L.b1 = take(m * D.d * D.e);
   L.z = take(m * D.Fp * D.e);
-  // Split-K partials are only used when a GEMM has fewer than 128 tiles; then
-  // splits * M * N <= (256 / tiles + 1) * tiles * BM * BN < 384 * 128 * 128.
+  // Split-K partials of the four k-row GEMMs: gemm_partial_bound(M, N) covers every plan with
+  // M <= B * k_max rows.
   size_t gp = 0;
-  const int Ms[1] = {(int)m};
-  for (int mm : Ms) {
-    if (mm <= 0) continue;
-    const int shapes[4][3] = {{D.dq + 2 * D.dkv, D.d, kEpiQKV}, {D.d, D.dq, kEpiResid},
-                              {2 * D.Fp, D.d, kEpiSwiGLU}, {D.d, D.Fp, kEpiResidScatter}};
-    for (auto &sh : shapes) {
-      const GemmPlan p = plan_gemm(D.dtype, mm, sh[0], sh[1], sh[2]);
-      if (p.splits > 1) {
-        const size_t b = gemm_partial_bytes(p, mm, sh[0]);
-        if (b > gp) gp = b;
-      }
+  if (m > 0) {
+    const int widths[4] = {D.dq + 2 * D.dkv, D.d, 2 * D.Fp, D.d};
+    for (int n : widths) {
+      const size_t b = gemm_partial_bound((int)m, n);
+      if (b > gp) gp = b;
     }
   }
-  const size_t bound = (D.dtype == SPA_BF16 ? 384ull * 128 * 128 : 384ull * 64 * 64) * 4;
-  if (m > 0 && gp < bound) gp = bound;
   L.gpart = take(gp);
   L.total = off;
   return L;

@@ -71,28 +71,30 @@ typedef struct {
   float norm_eps;      /* RMSNorm epsilon                                            */
 } spa_shape;
 
-/* Tile-packed weight layout. The GEMM weights below are passed packed, once per model, by
- * spa_pack_weight: a row-major [rows][cols] matrix (y = x W^T) is cut into blocks of 64 rows x 128
- * bytes (64 x 64 bf16, 64 x 32 fp32), each stored as one contiguous 8 KB run, so that a GEMM
- * workgroup streams its weight panel sequentially from HBM instead of reading 128-byte pieces of
- * 64 rows that lie cols * e bytes apart. Rows are zero-padded to a multiple of 128, columns to a
- * multiple of 64; block (i, j) sits at byte offset (i * cols_pad * e / 128 + j) * 8192.
+/* Fragment-packed weight layout. The GEMM weights below are passed packed, once per model, by
+ * spa_pack_weight: a row-major [rows][cols] matrix (y = x W^T) is cut into 1 KB blocks, one per
+ * (32-row block rb, K block kb) with 16 bf16 or 8 fp32 elements of K per block, stored at byte offset
+ * (rb * cols_pad / kbe + kb) * 1024 (kbe = 16 for bf16, 8 for fp32). Inside a block, the 16 bytes at
+ * l * 16 (l = 0..63) hold row 32 rb + l % 32 and K elements 16 kb + 8 (l / 32) + j, j = 0..7 (bf16)
+ * or 8 kb + 2 j + l / 32, j = 0..3 (fp32): the lane order of a 32x32 MFMA B operand, so a GEMM wave
+ * loads its weight fragments with one coalesced 16-byte load per lane and streams every panel
+ * sequentially. Rows are zero-padded to a multiple of 32, columns to a multiple of 64.
  * SPA_PACK_GATE_UP takes the [W_gate; W_up] matrix (2F rows) and emits 2 F_pad rows
- * (F_pad = ceil(F / 64) * 64) interleaved in groups of 64: 32 gate rows, then the 32 up rows of the
- * same hidden units. */
+ * (F_pad = ceil(F / 64) * 64) where 32-row block rb holds the gate rows of hidden units
+ * 16 rb .. 16 rb + 15 followed by the up rows of the same units. */
 typedef enum { SPA_PACK_PLAIN = 0, SPA_PACK_GATE_UP = 1 } spa_pack_kind;
 
 /* Bytes of a packed [rows][cols] matrix of `dtype`. Host only. cols % 16 == 0 (and F % 16 == 0 for
  * SPA_PACK_GATE_UP, where rows = 2F). */
 int spa_packed_weight_bytes(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, size_t *bytes_out);
 
-/* Pack a row-major device matrix into the tile-packed layout (device, spa_packed_weight_bytes bytes,
+/* Pack a row-major device matrix into the fragment-packed layout (device, spa_packed_weight_bytes bytes,
  * must not overlap src). Stream-ordered; offline, once per model. */
 int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src, void *dst,
                     hipStream_t stream);
 
 /* Layer weights (device, read-only). The block is pre-norm: RMSNorm(g_attn) -> QKV -> attention ->
- * W_o -> residual -> RMSNorm(g_ffn) -> SwiGLU -> W_down -> residual. Matrices are tile-packed. */
+ * W_o -> residual -> RMSNorm(g_ffn) -> SwiGLU -> W_down -> residual. Matrices are fragment-packed. */
 typedef struct {
   const void *w_r;        /* packed r x d: Lambda_r V_r^T of W_v diag(g_attn) ([PN] 关键设计 2)   */
   const void *w_qkv;      /* packed (d_q + 2 d_kv) x d: rows [W_q; W_k; W_v]                      */
@@ -161,7 +163,7 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
                          const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
                          void *ws, size_t ws_bytes, hipStream_t stream, spa_timing *timing);
 
-/* Phase 1 scores only ([PN] 整体框架 Phase 1; [GS] part 1), with w_r tile-packed (spa_pack_weight of
+/* Phase 1 scores only ([PN] 整体框架 Phase 1; [GS] part 1), with w_r fragment-packed (spa_pack_weight of
  * the r x d matrix): p_out = X W_r^T (B x N x r float32) and,
  * when p_cache is not NULL, scores_out = cosine(p, p^c) (B x N). Never writes p_cache.
  * p_out may be NULL when only scores are wanted; scores_out may be NULL when p_cache is. */

@@ -207,8 +207,9 @@ def test_offline_proxy_matches_oracle():
 def test_packed_weight_bytes(lib):
     from adaptive_hidden_state_amd import binding
     assert binding.spa_packed_weight_bytes("bf16", 12288, 4096) == 12288 * 4096 * 2
-    assert binding.spa_packed_weight_bytes("bf16", 100, 80) == 128 * 128 * 2          # rows to 128, cols to 64
-    assert binding.spa_packed_weight_bytes("f32", 16, 256) == 128 * 256 * 4
+    assert binding.spa_packed_weight_bytes("bf16", 100, 80) == 128 * 128 * 2          # rows to 32, cols to 64
+    assert binding.spa_packed_weight_bytes("bf16", 33, 64) == 64 * 64 * 2
+    assert binding.spa_packed_weight_bytes("f32", 16, 256) == 32 * 256 * 4
     assert binding.spa_packed_weight_bytes("bf16", 2 * 688, 256, 1) == 2 * 704 * 256 * 2   # gate/up: 2 F_pad rows
     out = ctypes.c_size_t(0)
     assert lib.spa_packed_weight_bytes(1, 100, 81, 0, ctypes.byref(out)) == -2          # cols % 16

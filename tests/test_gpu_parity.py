@@ -306,29 +306,41 @@ def test_dream_layer_step_full_size():
 
 
 def _pack_reference(w, kind, e):
-    """The tile-packed layout written out on the host: 64-row x 128-byte blocks, zero padding,
-    gate/up rows interleaved in groups of 64 (32 gate rows, then the 32 up rows of the same units)."""
+    """The fragment-packed layout written out on the host: one 1 KB block per (32-row block rb, K
+    block kb of 16 bf16 / 8 fp32 elements), rb-major; lane l of a block holds row 32 rb + l % 32 at
+    k = 16 kb + 8 (l // 32) + j, j < 8 (bf16) or k = 8 kb + 2 j + l // 32, j < 4 (fp32). Zero padding
+    to 32 rows and 64 columns; gate/up: block rb holds the gate rows of units 16 rb .. 16 rb + 15,
+    then the up rows of the same units."""
     rows, cols = w.shape
-    bke = 128 // e
     cols_pad = -(-cols // 64) * 64
     if kind == 1:
         f = rows // 2
         fp = -(-f // 64) * 64
         logical = np.zeros((2 * fp, cols), w.dtype)
         for r in range(2 * fp):
-            q, ww = divmod(r, 64)
-            j = q * 32 + (ww % 32)
-            if j < f:
-                logical[r] = w[j] if ww < 32 else w[f + j]
+            rb, ww = divmod(r, 32)
+            u = rb * 16 + ww % 16
+            if u < f:
+                logical[r] = w[u] if ww < 16 else w[f + u]
         rows_pad = 2 * fp
     else:
-        rows_pad = -(-rows // 128) * 128
+        rows_pad = -(-rows // 32) * 32
         logical = np.zeros((rows_pad, cols), w.dtype)
         logical[:rows] = w
     full = np.zeros((rows_pad, cols_pad), w.dtype)
     full[:, :cols] = logical
-    blocks = full.reshape(rows_pad // 64, 64, cols_pad // bke, bke).transpose(0, 2, 1, 3)
-    return blocks.reshape(-1)
+    bkf = 16 if e == 2 else 8
+    out = []
+    for rb in range(rows_pad // 32):
+        for kb in range(cols_pad // bkf):
+            for lane in range(64):
+                r = rb * 32 + lane % 32
+                if e == 2:
+                    ks = [16 * kb + 8 * (lane // 32) + j for j in range(8)]
+                else:
+                    ks = [8 * kb + 2 * j + lane // 32 for j in range(4)]
+                out.append(full[r, ks])
+    return np.concatenate(out)
 
 
 @pytest.mark.parametrize("dtype,rows,cols,kind", [("bf16", 200, 96, 0), ("bf16", 2 * 688, 256, 1),
