@@ -365,18 +365,18 @@ constexpr TileCfg kTiles[6] = {{128, 192}, {64, 192}, {128, 128}, {128, 64}, {64
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
 
-// Cost model of one launch in CU clocks, fitted to MI355X measurements of these kernels: a workgroup
-// costs its K range times the larger of its load time (weight panel from HBM, A tile mostly from L2)
-// and its MFMA time; workgroups run one per CU in rounds; split-K adds the fp32 partial round trip
-// and a second launch.
+// Cost model of one launch in CU clocks, fitted to MI355X measurements of this kernel at M = 256 and
+// 1024 (within ~10%): a workgroup costs its K range times its load time (weight panel from HBM, A
+// tile mostly from L2) plus its MFMA time, which overlap little at one wave per SIMD; workgroups run
+// one per CU in rounds; split-K adds the fp32 partial round trip (~2.6 TB/s) and a second launch.
 double plan_cost(int bm, int bn, int M, int N, int K, int splits, int kc) {
   const long long tiles = (long long)ceil_div(M, bm) * ceil_div(N, bn);
   const long long wgs = tiles * splits;
   const double rounds = (double)ceil_div_ll(wgs, kCUs);
   const double load = (bn + 0.5 * bm) / 14.0;
-  const double mfma = (double)bm * bn / 1638.0;
-  double t = rounds * kc * (load > mfma ? load : mfma);
-  if (splits > 1) t += (double)M * N * splits * 8.0 / (kCUs * 28.0) + 4000.0;
+  const double mfma = (double)bm * bn / 1660.0;
+  double t = rounds * kc * (load + mfma);
+  if (splits > 1) t += (double)M * N * splits * 0.00646 + 4200.0;
   return t;
 }
 }  // namespace
@@ -396,7 +396,7 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       if (splits > 1 && kc < 4 * bk) break;       // keep at least four slabs per split
       if (splits > 1 && (long long)ceil_div(M, tc.bm) * ceil_div(N, tc.bn) * splits > kMaxSplitWGs) break;
       double cost = plan_cost(tc.bm, tc.bn, M, N, K, splits, kc);
-      if (kind == kEpiPartial) cost -= (splits > 1) ? 4000.0 : 0.0;  // partials are the output anyway
+      if (kind == kEpiPartial && splits > 1) cost -= 4200.0;  // partials are the output anyway
       if (best.bm == 0 || cost < best_cost) {
         best_cost = cost;
         best.cfg = cfg;
