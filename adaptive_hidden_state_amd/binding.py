@@ -40,8 +40,7 @@ class spa_shape(ctypes.Structure):
 
 class spa_layer_weights(ctypes.Structure):
     _fields_ = [("w_r", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
-                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("g_attn", ctypes.c_void_p),
-                ("g_ffn", ctypes.c_void_p)]
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
 
 
 class spa_layer_cache(ctypes.Structure):
@@ -70,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "spa_budget": ([I32, I32, ctypes.c_double, ctypes.c_double, ctypes.c_double, I32, P, P], ctypes.c_int),
         "spa_packed_weight_bytes": ([I32, I32, I32, I32, ctypes.POINTER(SZ)], ctypes.c_int),
-        "spa_pack_weight": ([I32, I32, I32, I32, P, P, P], ctypes.c_int),
+        "spa_pack_weight": ([I32, I32, I32, I32, P, P, P, P], ctypes.c_int),
         "spa_workspace_bytes": ([P, I32, ctypes.POINTER(SZ)], ctypes.c_int),
         "spa_layer_full": ([P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_layer_step": ([P, P, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
@@ -140,14 +139,13 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 class DeviceWeights(NamedTuple):
-    """Layer weights on the device, in the layouts of spa_layer_weights."""
+    """Layer weights on the device, fragment-packed as spa_layer_weights wants them (the RMSNorm gains
+    folded into w_qkv and w_gate_up)."""
     w_r: object        # r x d
-    w_qkv: object      # (d_q + 2 d_kv) x d
+    w_qkv: object      # (d_q + 2 d_kv) x d, times diag(g_attn)
     w_o: object        # d x d_q
-    w_gate_up: object  # 2F x d
+    w_gate_up: object  # 2F x d, times diag(g_ffn)
     w_down: object     # d x F
-    g_attn: object     # d
-    g_ffn: object      # d
 
 
 class DeviceCache(NamedTuple):
@@ -160,7 +158,7 @@ class DeviceCache(NamedTuple):
 def _check_bytes(t, need: int, name: str):
     have = t.numel() * t.element_size()
     if have < need:
-        raise ValueError(f"{name} holds {have} bytes, needs {need} (weights must be tile-packed: spa_pack_weight)")
+        raise ValueError(f"{name} holds {have} bytes, needs {need} (weights must be fragment-packed: spa_pack_weight)")
 
 
 def _weights_struct(w: DeviceWeights, tdt, shape=None) -> spa_layer_weights:
@@ -172,8 +170,6 @@ def _weights_struct(w: DeviceWeights, tdt, shape=None) -> spa_layer_weights:
                 "w_down": (s.d_model, s.d_ffn, SPA_PACK_PLAIN)}
         for f, (r, c, kind) in need.items():
             _check_bytes(getattr(w, f), spa_packed_weight_bytes(s.dtype, r, c, kind), f)
-        for f in ("g_attn", "g_ffn"):
-            _check_bytes(getattr(w, f), s.d_model * getattr(w, f).element_size(), f)
     return spa_layer_weights(*(_ptr(getattr(w, f), tdt, f) for f in DeviceWeights._fields))
 
 
@@ -345,23 +341,28 @@ def spa_packed_weight_bytes(dtype, rows: int, cols: int, kind: int = SPA_PACK_PL
     return int(out.value)
 
 
-def spa_pack_weight(mat, kind: int = SPA_PACK_PLAIN, stream=None):
-    """Tile-packed copy (1-D device tensor) of a row-major device matrix [rows][cols] (y = x W^T)."""
+def spa_pack_weight(mat, kind: int = SPA_PACK_PLAIN, col_scale=None, stream=None):
+    """Fragment-packed copy (1-D device tensor) of a row-major device matrix [rows][cols] (y = x W^T),
+    optionally of W diag(col_scale) (col_scale: device vector of cols entries, same dtype)."""
     import torch
     if mat.dim() != 2:
         raise ValueError("weight must be a matrix")
     dt = "bf16" if mat.dtype == torch.bfloat16 else "f32"
     rows, cols = mat.shape
+    if col_scale is not None and (col_scale.dim() != 1 or col_scale.numel() != cols):
+        raise ValueError("col_scale must be a vector of one entry per column")
     nbytes = spa_packed_weight_bytes(dt, rows, cols, kind)
     dst = torch.empty(nbytes // mat.element_size(), dtype=mat.dtype, device=mat.device)
+    scale_ptr = None if col_scale is None else _ptr(col_scale, mat.dtype, "col_scale")
     _check(load_library().spa_pack_weight(dtype_code(dt), int(rows), int(cols), int(kind), _ptr(mat, None, "weight"),
-                                          _ptr(dst, None, "packed"), _stream(stream)), "spa_pack_weight")
+                                          scale_ptr, _ptr(dst, None, "packed"), _stream(stream)), "spa_pack_weight")
     return dst
 
 
 def upload_weights(w: dict, w_r, dtype, device="cuda") -> DeviceWeights:
-    """Device weights from host arrays (numpy or torch), packed for the GEMMs: [W_q; W_k; W_v],
-    W_o, [W_gate; W_up] (gate/up interleave), W_down and W_r; the gains stay plain vectors."""
+    """Device weights from host arrays (numpy or torch), packed for the GEMMs: [W_q; W_k; W_v] with the
+    attention RMSNorm gain folded in, W_o, [W_gate; W_up] (gate/up interleave) with the FFN RMSNorm gain
+    folded in, W_down and W_r."""
     import numpy as np
     import torch
     tdt = torch_dtype(dtype)
@@ -370,10 +371,13 @@ def upload_weights(w: dict, w_r, dtype, device="cuda") -> DeviceWeights:
         t = torch.as_tensor(np.ascontiguousarray(a, dtype=np.float32)) if not isinstance(a, torch.Tensor) else a
         return t.to(device=device, dtype=tdt).contiguous()
 
-    qkv = spa_pack_weight(torch.cat([dev(w["w_q"]), dev(w["w_k"]), dev(w["w_v"])], 0).contiguous())
-    gu = spa_pack_weight(torch.cat([dev(w["w_gate"]), dev(w["w_up"])], 0).contiguous(), SPA_PACK_GATE_UP)
+    g_attn, g_ffn = dev(w["g_attn"]), dev(w["g_ffn"])
+    qkv = spa_pack_weight(torch.cat([dev(w["w_q"]), dev(w["w_k"]), dev(w["w_v"])], 0).contiguous(),
+                          col_scale=g_attn)
+    gu = spa_pack_weight(torch.cat([dev(w["w_gate"]), dev(w["w_up"])], 0).contiguous(), SPA_PACK_GATE_UP,
+                         col_scale=g_ffn)
     out = DeviceWeights(spa_pack_weight(dev(w_r)), qkv, spa_pack_weight(dev(w["w_o"])), gu,
-                        spa_pack_weight(dev(w["w_down"])), dev(w["g_attn"]), dev(w["g_ffn"]))
+                        spa_pack_weight(dev(w["w_down"])))
     torch.cuda.current_stream().synchronize()   # the row-major staging copies are freed after packing
     return out
 

@@ -1,16 +1,19 @@
 // Partial cached attention ([PN] 整体框架 Phase 2): the k queries of the update set attend,
 // bidirectionally and without a mask, to all N keys of the (already scattered) K^c/V^c cache.
 //
-// One workgroup = one (sequence, query head, block of 32 queries) and four waves. The keys are split
-// into four contiguous ranges, one per wave; each wave runs an online softmax over its range and the
-// four partial results (running max, running sum, unnormalised output) are merged through LDS at the
-// end. Every wave streams its own key tiles (64 keys) through a private LDS region: K as [key][hd] and
-// V transposed to [hd][key], so that both products read contiguous LDS; no barrier is needed inside
-// the key loop (a wave's LDS accesses complete in order). A wave computes S^T = K Q^T (keys x queries)
-// on 32x32 MFMA blocks; in that layout a lane holds the scores of one query, so the softmax (fp32,
-// base-2 exponent) needs one cross-lane step, and the probabilities feed O^T = V^T P^T straight from
-// registers. V is transposed on the way into LDS: a lane loads an 8-key x 8-dim block (eight 16-byte
-// row pieces), transposes it in registers and writes eight 16-byte rows of V^T.
+// One workgroup = one (sequence, query head, block of 32 QG queries). Its waves form QG query groups
+// (32 queries each) x KR key ranges: the keys are split into KR contiguous ranges, each streamed in
+// tiles of 32 keys through a double-buffered LDS stage that the QG waves of the range load together
+// and all read, so every K/V byte fetched from L2 serves 32 QG queries. QG = 2 halves the L2 traffic
+// of QG = 1 but halves the number of workgroups; the launcher takes QG = 2 unless that would leave CUs
+// idle while QG = 1 fills them in one round. Each wave runs an online softmax over its range; the KR
+// partial results (running max, running sum, unnormalised output) of a query group are merged through
+// LDS at the end. K is staged as [key][hd] and V
+// transposed to [hd][key], so that both products read contiguous LDS. A wave computes S^T = K Q^T
+// (keys x queries) on 32x32 MFMA blocks; in that layout a lane holds the scores of one query, so the
+// softmax (fp32, base-2 exponent) needs one cross-lane step, and the probabilities feed O^T = V^T P^T
+// straight from registers. V is transposed on the way into LDS: a lane loads an 8-key x 8-dim block
+// (eight 16-byte row pieces), transposes it in registers and writes eight 16-byte rows of V^T.
 //
 // Workgroup ids are remapped so that each XCD (which receives every eighth workgroup) runs a
 // contiguous range of (sequence, KV head, query head, query block): the blocks that read the same K/V
@@ -37,43 +40,54 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 *in, u32x4 *out) {
   }
 }
 
-constexpr int kAttnWaves = 4;     // key ranges per workgroup
-constexpr int kAttnQueries = 32;  // queries per workgroup
-
-template <typename T, int HD> struct AttnCfg {
+template <typename T, int HD, int QG> struct AttnCfg {
+  static constexpr int Q = 32 * QG;                                // queries per workgroup
   static constexpr bool BF = sizeof(T) == 2;
-  static constexpr int KT = (BF || HD == 64) ? 64 : 32;            // keys per tile
+  static constexpr int KT = 32;                                    // keys per tile
   static constexpr int KROWB = HD * (int)sizeof(T) + 16;           // K tile row stride (bytes)
   static constexpr int VROWB = KT * (int)sizeof(T) + 16;           // V^T tile row stride (bytes)
-  static constexpr int WAVE_BYTES = KT * KROWB + HD * VROWB;       // private LDS of one wave
+  static constexpr int STAGE = KT * KROWB + HD * VROWB;            // one K + V^T tile
+  // Shared stages (QG > 1) are double-buffered with a barrier per tile; a key range owned by a single
+  // wave (QG = 1) has one private stage and needs no barrier (a wave's LDS accesses are in order).
+  static constexpr int NBUF = QG > 1 ? 2 : 1;
+  // key ranges: as many of 8, 4, 2 as fit in LDS, at most 8 waves per workgroup
+  static constexpr int KR0 = 8 / QG;
+  static constexpr int KR = NBUF * KR0 * STAGE <= 160 * 1024 ? KR0 : (NBUF * (KR0 / 2) * STAGE <= 160 * 1024 ? KR0 / 2 : KR0 / 4);
+  static constexpr int W = QG * KR;                                // waves per workgroup
   static constexpr int PROWB = (HD + 4) * 4;                       // merge buffer row (fp32 O of a query)
-  static_assert(kAttnQueries * PROWB + kAttnQueries * 8 <= WAVE_BYTES, "merge buffer fits a wave region");
-  static_assert(kAttnWaves * WAVE_BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int MERGE = 32 * PROWB + 32 * 8;                // one wave's partial state
+  static constexpr int LDS = NBUF * KR * STAGE;
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int TPQ = (64 * W / Q) < (HD / VEC) ? (64 * W / Q) : (HD / VEC);  // merge threads per query
+  static constexpr int SEG = HD / TPQ;                             // dims per merge thread
+  static_assert(W * MERGE <= LDS && LDS <= 160 * 1024, "LDS budget");
+  static_assert(SEG % VEC == 0, "whole 16-byte stores in the merge");
 };
 
-template <typename T, int HD>
-__global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
+template <typename T, int HD, int QG>
+__global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel(
     const T *__restrict__ q, const T *__restrict__ kc, const T *__restrict__ vc, T *__restrict__ o,
     int m_per_seq, int n_tok, int hq, int hkv, int qblocks, int nwg, float scale_log2) {
-  typedef AttnCfg<T, HD> C;
+  typedef AttnCfg<T, HD, QG> C;
+  constexpr int kAttnQG = QG, kAttnQueries = C::Q;
   constexpr bool BF = C::BF;
-  constexpr int KT = C::KT;
-  constexpr int NKB = KT / 32;                            // 32-key MFMA blocks per tile
+  constexpr int KT = C::KT, KR = C::KR;
   constexpr int KROWB = C::KROWB, VROWB = C::VROWB;
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int KCH = KT * HD / VEC / 64;                 // K 16-byte chunks per lane per tile
+  constexpr int VEC = C::VEC;
+  constexpr int KCH = KT * HD / VEC / (64 * kAttnQG);     // K 16-byte chunks per lane per tile
   // V: bf16 uses 8x8 blocks (8 key rows x one 16-byte chunk); fp32 uses 4x4 blocks
   constexpr int VB = BF ? 8 : 4;
   constexpr int VTASKS = (KT / VB) * (HD / VB);           // blocks per tile
-  constexpr int VPER = VTASKS / 64;
+  constexpr int VW = (VTASKS + kAttnQG - 1) / kAttnQG;    // blocks per wave of a key range
+  constexpr int VPER = (VW + 63) / 64;
   constexpr int QSTEPS = BF ? HD / 16 : HD / 2;           // MFMA k-steps over the head dim
   constexpr int KSTEP_B = BF ? 32 : 8;
   constexpr int LANE_B = BF ? 16 : 4;
   constexpr int HB = HD / 32;                             // 32-row blocks of the head dim
-  static_assert(KT * HD % (VEC * 64) == 0 && VTASKS % 64 == 0, "tile load split");
+  static_assert(KT * HD % (VEC * 64 * kAttnQG) == 0, "K tile load split");
   typedef typename AFrag<BF>::type FragT;
 
-  __shared__ __attribute__((aligned(16))) char smem[kAttnWaves * C::WAVE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   // XCD-aware order: hardware hands workgroup i to XCD i % 8
   const int nb = gridDim.x;
@@ -89,10 +103,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
   const int h = g * grp + h_in;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = qb * kAttnQueries;
+  const int qg = wave % kAttnQG, kr = wave / kAttnQG;
+  const int m0 = qb * kAttnQueries + qg * 32;
   const int ldq = hq * HD;
-  char *ks = smem + wave * C::WAVE_BYTES;
-  char *vts = ks + KT * KROWB;
+  auto stage = [&](int buf) { return smem + ((C::NBUF > 1 ? buf : 0) * KR + kr) * C::STAGE; };
 
   // Q fragments: B operand of S^T = K Q^T (column = query lane%32, k = head dim).
   FragT qf[QSTEPS];
@@ -119,27 +133,28 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
-  // This wave's tiles: [t_begin, t_begin + nt).
+  // Key range kr covers tiles [kr * tper, (kr + 1) * tper); every wave runs tper tiles (a barrier per
+  // tile), tiles past the end are clamped loads whose keys are all masked.
   const int ntiles = (n_tok + KT - 1) / KT;
-  const int tper = (ntiles + kAttnWaves - 1) / kAttnWaves;
-  const int t_begin = wave * tper;
-  const int nt = max(0, min(tper, ntiles - t_begin));
+  const int tper = (ntiles + KR - 1) / KR;
+  const int t_begin = kr * tper;
 
-  // V block assignment: block id v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so
+  // The QG waves of a key range split the tile loads: K chunks lane + 64 (j * QG + qg); V blocks
+  // qg * VW + lane + 64 p, block v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so
   // the lanes that write one V^T row segment hold consecutive key blocks (conflict-free LDS).
   u32x4 rk[KCH], rv[VPER][VB];
   auto gload = [&](int t) {  // rows past the end are clamped to the last key (masked later)
     const int key0 = t * KT;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = lane + j * 64;
+      const int c = lane + 64 * (j * kAttnQG + qg);
       const int row = c / (HD / VEC), col = c % (HD / VEC);
       const int key = min(key0 + row, n_tok - 1);
       rk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
     }
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
-      const int v = lane + p * 64;
+      const int v = min(qg * VW + min(lane + 64 * p, VW - 1), VTASKS - 1);
       const int kb = v % (KT / VB), cc = v / (KT / VB);
 #pragma unroll
       for (int j = 0; j < VB; ++j) {
@@ -148,16 +163,18 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
+    char *ks = stage(buf), *vts = ks + KT * KROWB;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = lane + j * 64;
+      const int c = lane + 64 * (j * kAttnQG + qg);
       const int row = c / (HD / VEC), col = c % (HD / VEC);
       st16(ks + row * KROWB + col * 16, rk[j]);
     }
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
-      const int v = lane + p * 64;
+      const int vi = lane + 64 * p, v = qg * VW + vi;
+      if (vi >= VW || v >= VTASKS) continue;
       const int kb = v % (KT / VB), cc = v / (KT / VB);
       if constexpr (BF) {
         u32x4 tr[8];
@@ -174,62 +191,41 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
     }
   };
 
-  auto compute = [&](int t) {
-    // S^T blocks of 32 keys: lane holds query lane%32 and keys
-    // kb*32 + 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15
-    floatx16 s[NKB];
+  auto compute = [&](int t, int buf) {
+    const char *ks = stage(buf), *vts = ks + KT * KROWB;
+    // S^T block of 32 keys: lane holds query lane%32 and keys 8*(r/4) + 4*(lane/32) + r%4, r = 0..15;
+    // two independent MFMA chains over the even and odd head-dim steps
+    floatx16 s, s2;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int r = 0; r < 16; ++r) s[r] = s2[r] = 0.f;
+    const char *krow = ks + (lane & 31) * KROWB + (lane >> 5) * LANE_B;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-    if constexpr (NKB == 2) {
-      // two independent MFMA chains: the two key blocks
-      const char *krow0 = ks + (lane & 31) * KROWB + (lane >> 5) * LANE_B;
-      const char *krow1 = krow0 + 32 * KROWB;
-#pragma unroll
-      for (int st = 0; st < QSTEPS; ++st) {
-        s[0] = mfma32(*reinterpret_cast<const FragT *>(krow0 + st * KSTEP_B), qf[st], s[0]);
-        s[1] = mfma32(*reinterpret_cast<const FragT *>(krow1 + st * KSTEP_B), qf[st], s[1]);
-      }
-    } else {
-      // one key block: two chains over the even and odd head-dim steps
-      floatx16 s2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s2[r] = 0.f;
-      const char *krow = ks + (lane & 31) * KROWB + (lane >> 5) * LANE_B;
-#pragma unroll
-      for (int st = 0; st < QSTEPS; st += 2) {
-        s[0] = mfma32(*reinterpret_cast<const FragT *>(krow + st * KSTEP_B), qf[st], s[0]);
-        s2 = mfma32(*reinterpret_cast<const FragT *>(krow + (st + 1) * KSTEP_B), qf[st + 1], s2);
-      }
-      s[0] += s2;
+    for (int st = 0; st < QSTEPS; st += 2) {
+      s = mfma32(*reinterpret_cast<const FragT *>(krow + st * KSTEP_B), qf[st], s);
+      s2 = mfma32(*reinterpret_cast<const FragT *>(krow + (st + 1) * KSTEP_B), qf[st + 1], s2);
     }
+    s += s2;
     // raw scores; the softmax scale (and log2 e) is applied inside one FMA per score
-    if (t * KT + KT > n_tok) {  // partial last tile (uniform branch): mask keys past the end
+    if (t * KT + KT > n_tok) {  // a tile reaching past the end (uniform branch): mask those keys
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * KT + kb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (key >= n_tok) s[kb][r] = -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * KT + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (key >= n_tok) s[r] = -INFINITY;
+      }
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kb][r]);
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
-    const float mnew = fmaxf(mrun, tmax);  // finite: a wave's first tile holds at least one key
+    const float mnew = fmaxf(mrun, tmax);
+    const float msub = mnew == -INFINITY ? 0.f : mnew;  // no key seen yet: every p is 0
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[kb][r], scale_log2, -mnew));
-        s[kb][r] = p;
-        psum += p;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2f(fmaf(s[r], scale_log2, -msub));
+      s[r] = p;
+      psum += p;
+    }
     // rescale the running sums only when some query of this wave raised its maximum
     if (__any(mnew > mrun)) {
       const float alpha = exp2f(mrun - mnew);
@@ -240,63 +236,63 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
     lrun += psum;
     mrun = mnew;
 
-    // O^T += V^T P^T. In k-step (kb, half) lane group G = lane/32 supplies its scores r = half*8..
-    // half*8+7, i.e. keys kb*32 + half*16 + {4G..4G+3, 8+4G..8+4G+3}; A = V^T rows at those keys.
+    // O^T += V^T P^T. In k-step `half` lane group G = lane/32 supplies its scores r = half*8..
+    // half*8+7, i.e. keys half*16 + {4G..4G+3, 8+4G..8+4G+3}; A = V^T rows at those keys.
     const int G = lane >> 5;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int half = 0; half < 2; ++half) {
+      if constexpr (BF) {
+        u32x4 pf;
+        pf[0] = pack_bf16x2(s[half * 8 + 0], s[half * 8 + 1]);
+        pf[1] = pack_bf16x2(s[half * 8 + 2], s[half * 8 + 3]);
+        pf[2] = pack_bf16x2(s[half * 8 + 4], s[half * 8 + 5]);
+        pf[3] = pack_bf16x2(s[half * 8 + 6], s[half * 8 + 7]);
+        const int c0 = (half * 16 + 4 * G) * 2, c1 = c0 + 16;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if constexpr (BF) {
-          u32x4 pf;
-          pf[0] = pack_bf16x2(s[kb][half * 8 + 0], s[kb][half * 8 + 1]);
-          pf[1] = pack_bf16x2(s[kb][half * 8 + 2], s[kb][half * 8 + 3]);
-          pf[2] = pack_bf16x2(s[kb][half * 8 + 4], s[kb][half * 8 + 5]);
-          pf[3] = pack_bf16x2(s[kb][half * 8 + 6], s[kb][half * 8 + 7]);
-          const int c0 = (kb * 32 + half * 16 + 4 * G) * 2, c1 = c0 + 16;
+        for (int hb = 0; hb < HB; ++hb) {
+          const char *vrow = vts + (hb * 32 + (lane & 31)) * VROWB;
+          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
+          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[hb] = mfma32(vf, pf, oacc[hb]);
+        }
+      } else {
+        // fp32 MFMA takes one key per lane group: MFMA r covers keys of score r for G = 0 and 1
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = half * 8 + i;
+          const int key = (r >> 2) * 8 + G * 4 + (r & 3);
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
-            const char *vrow = vts + (hb * 32 + (lane & 31)) * VROWB;
-            const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
-            const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-            oacc[hb] = mfma32(vf, pf, oacc[hb]);
-          }
-        } else {
-          // fp32 MFMA takes one key per lane group: MFMA r covers keys of score r for G = 0 and 1
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int r = half * 8 + i;
-            const int key = kb * 32 + (r >> 2) * 8 + G * 4 + (r & 3);
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-              const float vf = *reinterpret_cast<const float *>(vts + (hb * 32 + (lane & 31)) * VROWB + key * 4);
-              oacc[hb] = mfma32(vf, s[kb][r], oacc[hb]);
-            }
+            const float vf = *reinterpret_cast<const float *>(vts + (hb * 32 + (lane & 31)) * VROWB + key * 4);
+            oacc[hb] = mfma32(vf, s[r], oacc[hb]);
           }
         }
       }
+    }
   };
 
-  // One tile in registers ahead of the one in LDS. Branches depend only on the wave's tile count.
-  if (nt > 0) {
-    gload(t_begin);
-    lstore();
-    gload(t_begin + 1);
-    for (int i = 0; i < nt; ++i) {
-      compute(t_begin + i);
-      if (i + 1 < nt) {
-        lstore();
-        gload(t_begin + i + 2);
-      }
+  // Tile i + 1 is loaded into registers during tile i and written to the (other) stage after it; with
+  // shared stages one barrier per tile (every wave runs the same tper tiles).
+  gload(t_begin);
+  lstore(0);
+  gload(t_begin + 1);
+  if constexpr (QG > 1) __syncthreads();
+  for (int i = 0; i < tper; ++i) {
+    compute(t_begin + i, i & 1);
+    if (i + 1 < tper) {
+      lstore((i + 1) & 1);
+      gload(t_begin + i + 2);
     }
+    if constexpr (QG > 1) __syncthreads();
   }
+  if constexpr (QG == 1) __syncthreads();  // the merge below overwrites other waves' stages
 
-  // Merge the four key ranges. Each wave parks its partial state in its own LDS region (whose K/V
-  // tiles only it reads), then all threads combine.
+  // Merge the key ranges of each query group. Every wave parks its partial state in LDS (the stages
+  // are free after the last barrier), then all threads combine.
   lrun += __shfl_xor(lrun, 32, kWave);
   {
-    char *part = ks;
+    char *part = smem + wave * C::MERGE;
     const int G = lane >> 5;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -305,49 +301,51 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
         *reinterpret_cast<floatx4 *>(part + (lane & 31) * C::PROWB + (hb * 32 + r4 * 8 + G * 4) * 4) =
             floatx4{oacc[hb][r4 * 4 + 0], oacc[hb][r4 * 4 + 1], oacc[hb][r4 * 4 + 2], oacc[hb][r4 * 4 + 3]};
     if (lane < 32) {
-      float *ml = reinterpret_cast<float *>(part + kAttnQueries * C::PROWB);
+      float *ml = reinterpret_cast<float *>(part + 32 * C::PROWB);
       ml[2 * lane] = mrun;
       ml[2 * lane + 1] = lrun;
     }
   }
   __syncthreads();
   {
-    constexpr int SEG = HD / 8;  // dims per thread: 8 threads per query
-    const int qi = tid >> 3, d0 = (tid & 7) * SEG;
-    float mw[kAttnWaves], lw[kAttnWaves];
+    constexpr int SEG = C::SEG, TPQ = C::TPQ;
+    const int qi = tid / TPQ, d0 = (tid % TPQ) * SEG;  // query qi of the block: group qi / 32
+    if (qi >= kAttnQueries) return;                    // after the last barrier
+    const int gq = qi >> 5, ql = qi & 31;
+    float mw[KR], lw[KR];
     float mmax = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const float *ml = reinterpret_cast<const float *>(smem + w * C::WAVE_BYTES + kAttnQueries * C::PROWB);
-      mw[w] = ml[2 * qi];
-      lw[w] = ml[2 * qi + 1];
-      mmax = fmaxf(mmax, mw[w]);
+    for (int r = 0; r < KR; ++r) {
+      const float *ml = reinterpret_cast<const float *>(smem + (r * kAttnQG + gq) * C::MERGE + 32 * C::PROWB);
+      mw[r] = ml[2 * ql];
+      lw[r] = ml[2 * ql + 1];
+      mmax = fmaxf(mmax, mw[r]);
     }
-    float aw[kAttnWaves], lsum = 0.f;
+    float aw[KR], lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      aw[w] = mw[w] == -INFINITY ? 0.f : exp2f(mw[w] - mmax);  // a wave without keys adds nothing
-      lsum = fmaf(aw[w], lw[w], lsum);
+    for (int r = 0; r < KR; ++r) {
+      aw[r] = mw[r] == -INFINITY ? 0.f : exp2f(mw[r] - mmax);  // a range without keys adds nothing
+      lsum = fmaf(aw[r], lw[r], lsum);
     }
     const float inv = 1.0f / lsum;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) aw[w] *= inv;
+    for (int r = 0; r < KR; ++r) aw[r] *= inv;
     float acc[SEG];
 #pragma unroll
     for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const char *row = smem + w * C::WAVE_BYTES + qi * C::PROWB + d0 * 4;
+    for (int r = 0; r < KR; ++r) {
+      const char *row = smem + (r * kAttnQG + gq) * C::MERGE + ql * C::PROWB + d0 * 4;
 #pragma unroll
       for (int e = 0; e < SEG; e += 4) {
         const floatx4 v = *reinterpret_cast<const floatx4 *>(row + e * 4);
-        acc[e] = fmaf(aw[w], v[0], acc[e]);
-        acc[e + 1] = fmaf(aw[w], v[1], acc[e + 1]);
-        acc[e + 2] = fmaf(aw[w], v[2], acc[e + 2]);
-        acc[e + 3] = fmaf(aw[w], v[3], acc[e + 3]);
+        acc[e] = fmaf(aw[r], v[0], acc[e]);
+        acc[e + 1] = fmaf(aw[r], v[1], acc[e + 1]);
+        acc[e + 2] = fmaf(aw[r], v[2], acc[e + 2]);
+        acc[e + 3] = fmaf(aw[r], v[3], acc[e + 3]);
       }
     }
-    const int qo = m0 + qi;
+    const int qo = qb * kAttnQueries + qi;
     if (qo < m_per_seq) {
       T *dst = o + ((size_t)b * m_per_seq + qo) * ldq + (size_t)h * HD + d0;
 #pragma unroll
@@ -361,18 +359,29 @@ __global__ __launch_bounds__(64 * kAttnWaves) void attention_kernel(
   }
 }
 
-template <typename T, int HD>
-static hipError_t run_attention(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
-                                int n_tok, int hq, int hkv, hipStream_t s) {
+template <typename T, int HD, int QG>
+static hipError_t launch_qg(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
+                            int n_tok, int hq, int hkv, hipStream_t s) {
+  typedef AttnCfg<T, HD, QG> C;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  const int qblocks = (m_per_seq + kAttnQueries - 1) / kAttnQueries;
+  const int qblocks = (m_per_seq + C::Q - 1) / C::Q;
   const long long nwg = (long long)qblocks * hq * batch;
   if (nwg > (1LL << 30)) return hipErrorInvalidValue;
   const int grid = (int)((nwg + 7) / 8 * 8);
-  hipLaunchKernelGGL((attention_kernel<T, HD>), dim3(grid), dim3(64 * kAttnWaves), 0, s, (const T *)q,
+  hipLaunchKernelGGL((attention_kernel<T, HD, QG>), dim3(grid), dim3(64 * C::W), 0, s, (const T *)q,
                      (const T *)kc, (const T *)vc, (T *)o, m_per_seq, n_tok, hq, hkv, qblocks, (int)nwg,
                      scale_log2);
   return hipGetLastError();
+}
+
+template <typename T, int HD>
+static hipError_t run_attention(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
+                                int n_tok, int hq, int hkv, hipStream_t s) {
+  constexpr int kCUs = 256;
+  const long long heads = (long long)hq * batch;
+  const long long wg64 = heads * ((m_per_seq + 63) / 64), wg32 = heads * ((m_per_seq + 31) / 32);
+  if (wg64 < kCUs && wg32 <= kCUs) return launch_qg<T, HD, 1>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  return launch_qg<T, HD, 2>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
 }
 
 hipError_t launch_attention(int dtype, const void *q, const void *kc, const void *vc, void *o, int batch,

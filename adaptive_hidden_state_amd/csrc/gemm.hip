@@ -120,8 +120,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
   static_assert(FM % 2 == 0 && FN >= 1 && BM * 8 % 256 == 0, "tile shape");
   static_assert(PF == 2 || PF == 4, "prefetch depth must be even");
   typedef GemmLds<BM, BN> L;
+  constexpr bool NORM = KIND == kEpiQKV || KIND == kEpiSwiGLU;  // A is RMSNorm's input (never split)
 
   __shared__ __attribute__((aligned(16))) char lds[L::kBytes];
+  __shared__ float row_scale[NORM ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wk = wave >> 1;
@@ -142,10 +144,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll
   for (int j = 0; j < A_PER; ++j) {
     const int c = tid + j * 256, row = c >> 3, col = c & 7;
-    const int gr = min(tm * BM + row, M - 1);
-    a_src[j] = reinterpret_cast<const char *>(A + (size_t)gr * lda + k0) + col * 16;
+    const int m = min(tm * BM + row, M - 1);
+    size_t gr = (size_t)m;
+    if (NORM && ea.idx != nullptr) {  // A rows gathered through the update set
+      int b;
+      const int i = map_token(ea, m, b);
+      gr = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+    }
+    a_src[j] = reinterpret_cast<const char *>(A + gr * lda + k0) + col * 16;
     a_dst[j] = row * ROWB + col * 16;
   }
+  // fused RMSNorm: this thread's share (16 bytes per slab) of the sum of squares of its A rows
+  float ssq[A_PER];
+#pragma unroll
+  for (int j = 0; j < A_PER; ++j) ssq[j] = 0.f;
   // B: this wave's column blocks, blocks 2 wk and 2 wk + 1 of every slab (four blocks per slab)
   const int cb0 = (tn * BN + wn * (BN / 2)) / 32;
   const int cb_last = (N + 31) / 32 - 1;
@@ -157,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
   }
 
   // Register ring of PF K slabs in flight: slab kt lives in slot kt % PF from its load until its A part
-  // is written to LDS (one iteration before use) and its B fragments are consumed. Loads are
+  // is written to LDS (at the start of the iteration before its use) and its B fragments are consumed. Loads are
   // unconditional (the slab index is clamped), so the compiler waits for exactly the oldest slab; the
   // slab count is padded to a multiple of PF and padding slabs enter LDS with A zeroed.
   u32x4 ra[PF][A_PER], rb[PF][2 * FN];
@@ -176,7 +188,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
     char *dst = lds + buf * BM * ROWB;
     if (kt < nk) {
 #pragma unroll
-      for (int j = 0; j < A_PER; ++j) st16(dst + a_dst[j], xa[j]);
+      for (int j = 0; j < A_PER; ++j) {
+        st16(dst + a_dst[j], xa[j]);
+        if constexpr (NORM) {
+          if constexpr (BF) {  // exact fp32 squares (bf16 -> fp32 is a shift), fp32 accumulation
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const float lo = __uint_as_float(xa[j][x] << 16), hi = __uint_as_float(xa[j][x] & 0xffff0000u);
+              ssq[j] = fmaf(lo, lo, ssq[j]);
+              ssq[j] = fmaf(hi, hi, ssq[j]);
+            }
+          } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ssq[j] = fmaf(__uint_as_float(xa[j][x]), __uint_as_float(xa[j][x]), ssq[j]);
+          }
+        }
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < A_PER; ++j) st16(dst + a_dst[j], zero);
@@ -204,6 +231,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int kt = kt0 + u;
+      // stage slab kt + 1 into the other buffer first (its VALU work then precedes the MFMA burst)
+      lstore((u + 1) & 1, kt + 1, ra[(u + 1) % PF]);
       const char *As = lds + (u & 1) * BM * ROWB + frag_off;  // PF is even: slab kt0 + u is in buffer u & 1
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -228,10 +257,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
               for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], __uint_as_float(rb[u][2 * j + t][s]), acc[i][j]);
           }
         }
-      const int nslot = (u + 1) % PF;
-      lstore((u + 1) & 1, kt + 1, ra[nslot]);
       gload(kt + PF, ra[u], rb[u]);
       __syncthreads();
+    }
+  }
+
+  if constexpr (NORM) {  // 8 consecutive lanes share a row; lane 0 of the 8 writes 1 / rms
+#pragma unroll
+    for (int j = 0; j < A_PER; ++j) {
+      float v = ssq[j];
+      v += __shfl_xor(v, 1, kWave);
+      v += __shfl_xor(v, 2, kWave);
+      v += __shfl_xor(v, 4, kWave);
+      if ((tid & 7) == 0) row_scale[(tid + j * 256) >> 3] = 1.0f / sqrtf(v / (float)ea.norm_d + ea.norm_eps);
     }
   }
 
@@ -300,13 +338,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
       const int c = g8 >> 1, h = g8 & 1;
       const int m = mbase + lr, j0 = (nbase / 32 + c) * 16 + h * 8;
       const float *row = ep + lr * ES + c * 32 + h * 8;
-      if (m < M && j0 < ea.f) epi8_swiglu<T>(ea, m, j0, row, row + 16);
+      if (m < M && j0 < ea.f) {
+        float g[8], u[8];
+        const float sc = NORM ? row_scale[wk * ER + lr] : 1.0f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          g[x] = row[x] * sc;
+          u[x] = row[16 + x] * sc;
+        }
+        epi8_swiglu<T>(ea, m, j0, g, u);
+      }
     }
   } else {
     for (int idx = lane; idx < ER * EC / 8; idx += 64) {
       const int lr = idx / (EC / 8), c8 = idx - lr * (EC / 8);
       const int m = mbase + lr, n0 = nbase + c8 * 8;
-      if (m < M && n0 < N) epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
+      if (m < M && n0 < N) {
+        if constexpr (NORM) {
+          float v[8];
+          const float sc = row_scale[wk * ER + lr];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) v[x] = ep[lr * ES + c8 * 8 + x] * sc;
+          epi8<T, KIND>(ea, m, n0, v);
+        } else {
+          epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
+        }
+      }
     }
   }
 }
@@ -393,6 +450,7 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       int kc = ceil_div(ceil_div(K, s), bk) * bk;
       const int splits = ceil_div(K, kc);
       if (splits != s) continue;                  // duplicate of a smaller split count
+      if (splits > 1 && (kind == kEpiQKV || kind == kEpiSwiGLU)) break;  // fused RMSNorm needs all of K
       if (splits > 1 && kc < 4 * bk) break;       // keep at least four slabs per split
       if (splits > 1 && (long long)ceil_div(M, tc.bm) * ceil_div(N, tc.bn) * splits > kMaxSplitWGs) break;
       double cost = plan_cost(tc.bm, tc.bn, M, N, K, splits, kc);

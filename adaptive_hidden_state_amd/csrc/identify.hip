@@ -17,28 +17,36 @@ constexpr int kMaxSplits = 16;       // the proxy GEMM never splits K more than 
 __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
                                                            int r, const float *pc_read, float *pc_write,
                                                            float *__restrict__ p_out, float *__restrict__ scores) {
+  // one wave per row, four consecutive columns per lane per chunk (16-byte accesses; r % 16 == 0)
+  constexpr int kChunks = kMaxRankPerLane / 4;  // r <= 1024: 4 chunks of 64 lanes x 4 columns
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const size_t plane = (size_t)rows * r;
   const size_t base = (size_t)row * r;
-  float p[kMaxRankPerLane];
+  floatx4 p[kChunks];
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxRankPerLane; ++c) {
-    const int col = lane + 64 * c;
-    float v = 0.f;
+  for (int c = 0; c < kChunks; ++c) {
+    const int col = (lane + 64 * c) * 4;
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
     if (col < r) {
-      float ps[kMaxSplits];
+      floatx4 ps[kMaxSplits];
 #pragma unroll
-      for (int s = 0; s < kMaxSplits; ++s) ps[s] = s < splits ? part[s * plane + base + col] : 0.f;
+      for (int sp = 0; sp < kMaxSplits; ++sp)
+        ps[sp] = sp < splits ? *reinterpret_cast<const floatx4 *>(part + sp * plane + base + col)
+                             : floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < kMaxSplits; ++s) v += ps[s];
-      n1 += v * v;
+      for (int sp = 0; sp < kMaxSplits; ++sp) v += ps[sp];  // fixed split order: deterministic
+#pragma unroll
+      for (int x = 0; x < 4; ++x) n1 += v[x] * v[x];
       if (pc_read != nullptr) {
-        const float w = pc_read[base + col];
-        dot += v * w;
-        n2 += w * w;
+        const floatx4 w = *reinterpret_cast<const floatx4 *>(pc_read + base + col);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          dot += v[x] * w[x];
+          n2 += w[x] * w[x];
+        }
       }
     }
     p[c] = v;
@@ -50,11 +58,11 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
     if (lane == 0) scores[row] = dot / (fmaxf(sqrtf(n1), 1e-8f) * fmaxf(sqrtf(n2), 1e-8f));
   }
 #pragma unroll
-  for (int c = 0; c < kMaxRankPerLane; ++c) {
-    const int col = lane + 64 * c;
+  for (int c = 0; c < kChunks; ++c) {
+    const int col = (lane + 64 * c) * 4;
     if (col < r) {
-      if (p_out != nullptr) p_out[base + col] = p[c];
-      if (pc_write != nullptr) pc_write[base + col] = p[c];
+      if (p_out != nullptr) *reinterpret_cast<floatx4 *>(p_out + base + col) = p[c];
+      if (pc_write != nullptr) *reinterpret_cast<floatx4 *>(pc_write + base + col) = p[c];
     }
   }
 }
@@ -81,15 +89,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over a wave with DPP: shifts of 1, 2, 4, 8 inside each 16-lane row, then the
+// row totals are carried into rows 1 and 3 (row_bcast:15) and into rows 2 and 3 (row_bcast:31).
+// Lanes without a source read 0 (bound_ctrl) or are masked off, which adds nothing.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)x;
+}
+
 // Exclusive prefix sum over the workgroup (1024 threads = 16 waves); wsum holds 16 entries.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, off, kWave);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t base = 0;
@@ -98,77 +115,134 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
   return base + x - v;
 }
 
+// AND / OR over a wave: rotations inside each 16-lane row (DPP row_ror), then the four row results.
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  int x = (int)v;
+  x &= __builtin_amdgcn_update_dpp(x, x, 0x121, 0xf, 0xf, false);  // row_ror:1
+  x &= __builtin_amdgcn_update_dpp(x, x, 0x122, 0xf, 0xf, false);  // row_ror:2
+  x &= __builtin_amdgcn_update_dpp(x, x, 0x124, 0xf, 0xf, false);  // row_ror:4
+  x &= __builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  return (uint32_t)(__builtin_amdgcn_readlane(x, 0) & __builtin_amdgcn_readlane(x, 16) &
+                    __builtin_amdgcn_readlane(x, 32) & __builtin_amdgcn_readlane(x, 48));
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  int x = (int)v;
+  x |= __builtin_amdgcn_update_dpp(x, x, 0x121, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(x, x, 0x122, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(x, x, 0x124, 0xf, 0xf, false);
+  x |= __builtin_amdgcn_update_dpp(x, x, 0x128, 0xf, 0xf, false);
+  return (uint32_t)(__builtin_amdgcn_readlane(x, 0) | __builtin_amdgcn_readlane(x, 16) |
+                    __builtin_amdgcn_readlane(x, 32) | __builtin_amdgcn_readlane(x, 48));
+}
+
+// Radix select of the k smallest keys, emitted in ascending index order. The bits every key shares
+// are skipped first (scores of one step often share sign, exponent and leading mantissa bits, which
+// would otherwise pile every key into one histogram bin); the rest is resolved with digits of up to
+// 11 bits, stopping as soon as the selected bin fits exactly. Equal keys at the boundary are taken in
+// index order.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int n, int k,
                                                             int32_t *__restrict__ idx_out) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[16];
-  __shared__ uint32_t sel_prefix, sel_krem;
+  constexpr int kBins = 2048;
+  __shared__ uint32_t hist[2][kBins];
+  __shared__ uint32_t wsum[16], wand[16], wor[16];
+  __shared__ uint32_t sel_prefix, sel_krem, sel_full;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *s = scores + (size_t)b * n;
+  int32_t *out = idx_out + (size_t)b * k;
   const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
   const int start = tid * chunk;
+  if (k >= n) {  // every token
+    for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
+    return;
+  }
 
   uint32_t key[kTopkPerThread];
-  uint32_t valid = 0;
+  uint32_t valid = 0, kand = 0xffffffffu, kor = 0u;
 #pragma unroll
   for (int j = 0; j < kTopkPerThread; ++j) {
     const int i = start + j;
     const bool ok = j < chunk && i < n;
     key[j] = ok ? order_key(s[i]) : 0u;
     valid |= (ok ? 1u : 0u) << j;
+    if (ok) {
+      kand &= key[j];
+      kor |= key[j];
+    }
   }
-
-  // Radix select (8 bits per pass, most significant first) of the k-th smallest key.
-  uint32_t prefix = 0, krem = (uint32_t)k;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  for (int i = tid; i < 2 * kBins; i += kTopkThreads) (&hist[0][0])[i] = 0u;
+  kand = wave_and(kand);
+  kor = wave_or(kor);
+  if (lane == 0) {
+    wand[wave] = kand;
+    wor[wave] = kor;
+  }
+  __syncthreads();
+  kand = 0xffffffffu;
+  kor = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    kand &= wand[w];
+    kor |= wor[w];
+  }
+  // bits above `hi` are common to every key
+  int hi = 31 - __clz(kand ^ kor);  // -1 when all keys are equal
+  uint32_t prefix = hi >= 31 ? 0u : (kand & (0xffffffffu << (hi + 1)));
+  uint32_t krem = (uint32_t)k;
+  bool full = false;
+  int pass = 0;
+  while (hi >= 0) {
+    const int lo = hi >= 10 ? hi - 10 : 0;
+    const uint32_t above = hi >= 31 ? 0u : (0xffffffffu << (hi + 1));
+    const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+    uint32_t *h = hist[pass & 1];
 #pragma unroll
     for (int j = 0; j < kTopkPerThread; ++j)
-      if (((valid >> j) & 1u) && (key[j] & hmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+      if (((valid >> j) & 1u) && (key[j] & above) == prefix) atomicAdd(&h[(key[j] >> lo) & dmask], 1u);
     __syncthreads();
-    uint32_t v = 0, incl = 0;
-    if (tid < 256) {
-      v = hist[tid];
-      incl = v;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)incl, off, kWave);
-        if (lane >= off) incl += y;
-      }
-      if (lane == 63) wsum[wave] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      for (int w = 0; w < wave; ++w) incl += wsum[w];
-      const uint32_t excl = incl - v;
-      if (excl < krem && krem <= incl) {
-        sel_prefix = prefix | ((uint32_t)tid << shift);
-        sel_krem = krem - excl;
-      }
+    // two bins per thread; inclusive counts by a block scan
+    const uint32_t v0 = h[2 * tid], v1 = h[2 * tid + 1];
+    uint32_t *hn = hist[(pass + 1) & 1];  // next pass's bins (last read one pass ago)
+    hn[2 * tid] = 0u;
+    hn[2 * tid + 1] = 0u;
+    const uint32_t e0 = block_exclusive_scan(v0 + v1, wsum);
+    const uint32_t i0 = e0 + v0, i1 = i0 + v1;
+    if (e0 < krem && krem <= i0) {
+      sel_prefix = prefix | ((uint32_t)(2 * tid) << lo);
+      sel_krem = krem - e0;
+      sel_full = (i0 == krem) ? 1u : 0u;
+    } else if (i0 < krem && krem <= i1) {
+      sel_prefix = prefix | ((uint32_t)(2 * tid + 1) << lo);
+      sel_krem = krem - i0;
+      sel_full = (i1 == krem) ? 1u : 0u;
     }
     __syncthreads();
     prefix = sel_prefix;
     krem = sel_krem;
+    full = sel_full != 0u;
     __syncthreads();
+    hi = lo - 1;
+    ++pass;
+    if (full) break;
   }
 
-  // Emit in index order: every key below the threshold, and the first `krem` keys equal to it.
-  const uint32_t thr = prefix;
-  uint32_t ceq = 0;
+  // Emit in index order: keys whose resolved bits are below the prefix, plus those equal to it --
+  // all of them when the last bin fitted exactly, else the first `krem` in index order.
+  const uint32_t mask = hi >= 31 ? 0u : (0xffffffffu << (hi + 1));
+  uint32_t r = 0;
+  if (!full) {
+    uint32_t ceq = 0;
 #pragma unroll
-  for (int j = 0; j < kTopkPerThread; ++j) ceq += (((valid >> j) & 1u) && key[j] == thr) ? 1u : 0u;
-  uint32_t r = block_exclusive_scan(ceq, wsum);
+    for (int j = 0; j < kTopkPerThread; ++j) ceq += (((valid >> j) & 1u) && (key[j] & mask) == prefix) ? 1u : 0u;
+    r = block_exclusive_scan(ceq, wsum);
+  }
   uint32_t sel = 0, csel = 0;
 #pragma unroll
   for (int j = 0; j < kTopkPerThread; ++j) {
     if (!((valid >> j) & 1u)) continue;
-    bool take = key[j] < thr;
-    if (key[j] == thr) {
-      take = r < krem;
+    const uint32_t km = key[j] & mask;
+    bool take = km < prefix;
+    if (km == prefix) {
+      take = full || r < krem;
       ++r;
     }
     if (take) {
@@ -177,7 +251,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     }
   }
   uint32_t pos = block_exclusive_scan(csel, wsum);
-  int32_t *out = idx_out + (size_t)b * k;
 #pragma unroll
   for (int j = 0; j < kTopkPerThread; ++j)
     if (((sel >> j) & 1u) && pos < (uint32_t)k) out[pos++] = start + j;
@@ -208,70 +281,6 @@ hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *id
   if (batch <= 0 || k <= 0) return hipSuccess;
   const int waves = batch * k;
   hipLaunchKernelGGL(copy_selected_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, p_src, pc, idx, batch, n, k, r);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------------------------
-// RMSNorm of (gathered) rows: dst[m] = x / sqrt(mean(x^2) + eps) * g; one wave per row.
-// ---------------------------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const T *__restrict__ src, const int32_t *__restrict__ idx,
-                                                      int k_per_seq, int n_tok, int rows, int d,
-                                                      const T *__restrict__ g, float eps, T *__restrict__ dst) {
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int MAXV = 16;  // 16-byte vectors per lane held in registers: d <= 1024 * VEC
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= rows) return;
-  size_t srow = (size_t)m;
-  if (idx != nullptr) {
-    const int b = m / k_per_seq;
-    const int i = min(max(idx[m], 0), n_tok - 1);
-    srow = (size_t)b * n_tok + i;
-  }
-  const T *x = src + srow * d;
-  T *y = dst + (size_t)m * d;
-  const int nvec = d / VEC;
-  u32x4 xv[MAXV];
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int v = lane + 64 * j;
-    xv[j] = v < nvec ? ld16(x + v * VEC) : u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    float f[VEC];
-    unpack16(xv[j], f, (const T *)nullptr);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) ss += f[e] * f[e];
-  }
-  ss = wave_sum(ss);
-  const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-  for (int j = 0; j < MAXV; ++j) {
-    const int v = lane + 64 * j;
-    if (v < nvec) {
-      float f[VEC], w[VEC];
-      unpack16(xv[j], f, (const T *)nullptr);
-      unpack16(ld16(g + v * VEC), w, (const T *)nullptr);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) f[e] = f[e] * rinv * w[e];
-      st16(y + v * VEC, pack16(f, (const T *)nullptr));
-    }
-  }
-}
-
-hipError_t launch_rmsnorm(int dtype, const void *src, const int32_t *idx, int k_per_seq, int n_tok, int rows, int d,
-                          const void *g, float eps, void *dst, hipStream_t s) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 grid((rows + 3) / 4);
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t *)src, idx, k_per_seq, n_tok,
-                       rows, d, (const bf16_t *)g, eps, (bf16_t *)dst);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, (const float *)src, idx, k_per_seq, n_tok,
-                       rows, d, (const float *)g, eps, (float *)dst);
   return hipGetLastError();
 }
 

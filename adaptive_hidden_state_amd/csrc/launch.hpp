@@ -32,6 +32,11 @@ struct EpiArgs {
   int ld_src;
   int ldo;
   int f;
+  // RMSNorm fused into the A operand (kinds kEpiQKV and kEpiSwiGLU): A rows are the raw hidden rows
+  // (gathered through idx when it is set), the RMSNorm gain is folded into the packed weight, and
+  // each output row is scaled by 1 / sqrt(mean(a^2) + norm_eps) over the norm_d columns of A.
+  int norm_d;
+  float norm_eps;
 };
 
 struct GemmPlan {
@@ -75,7 +80,9 @@ inline void packed_dims(int kind, int rows, int cols, int *rows_pad, int *cols_p
   *cols_pad = pad_to(cols, 64);
 }
 inline int packed_wkb(int dtype, int cols) { return pad_to(cols, 64) / (dtype == kBF16 ? 16 : 8); }
-hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const void *src, void *dst, hipStream_t s);
+// col_scale (nullable, cols entries of the matrix dtype): pack W diag(col_scale), rounded once.
+hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const void *src, const void *col_scale,
+                              void *dst, hipStream_t s);
 
 // Phase 1 pieces.
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,
@@ -83,10 +90,6 @@ hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, c
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s);
 hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *idx, int batch, int n,
                                 int k, int r, hipStream_t s);
-
-// RMSNorm of rows (optionally gathered through an update set) into a dense M x d buffer.
-hipError_t launch_rmsnorm(int dtype, const void *src, const int32_t *idx, int k_per_seq, int n_tok,
-                          int rows, int d, const void *g, float eps, void *dst, hipStream_t s);
 
 // Sparse-query attention: q (B*m_per_seq x hq*hd) against K^c/V^c (B x hkv x n_tok x hd).
 hipError_t launch_attention(int dtype, const void *q, const void *kc, const void *vc, void *o, int batch,

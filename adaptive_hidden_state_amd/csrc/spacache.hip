@@ -67,7 +67,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace regions. Offsets are multiples of 256 bytes.
 struct Layout {
   GemmPlan proxy;
-  size_t ppart, pbuf, scores, a1, q, o, y, b1, z, gpart, total;
+  size_t ppart, pbuf, scores, q, o, y, z, gpart, total;
 };
 
 Layout make_layout(const Dims &D, int k_max) {
@@ -84,11 +84,9 @@ Layout make_layout(const Dims &D, int k_max) {
   L.ppart = take(gemm_partial_bytes(L.proxy, (int)rows, D.r));
   L.pbuf = take(rows * D.r * 4);
   L.scores = take(rows * 4);
-  L.a1 = take(m * D.d * D.e);
   L.q = take(m * D.dq * D.e);
   L.o = take(m * D.dq * D.e);
   L.y = take(m * D.d * D.e);
-  L.b1 = take(m * D.d * D.e);
   L.z = take(m * D.Fp * D.e);
   // Split-K partials of the four k-row GEMMs: gemm_partial_bound(M, N) covers every plan with
   // M <= B * k_max rows.
@@ -134,7 +132,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SPA_OK : SPA_ERR_HIP; }
 
 int check_weights(const spa_layer_weights *w) {
   if (w == nullptr) return SPA_ERR_INVALID_ARG;
-  const void *p[7] = {w->w_r, w->w_qkv, w->w_o, w->w_gate_up, w->w_down, w->g_attn, w->g_ffn};
+  const void *p[5] = {w->w_r, w->w_qkv, w->w_o, w->w_gate_up, w->w_down};
   for (const void *x : p) {
     if (x == nullptr) return SPA_ERR_INVALID_ARG;
     if (!aligned16(x)) return SPA_ERR_ALIGN;
@@ -191,13 +189,10 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
                const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s, Marks &mk) {
   const int M = D.B * k_per_seq;
   if (M == 0) return SPA_OK;
-  void *a1 = at(ws, L.a1), *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *b1 = at(ws, L.b1),
-       *z = at(ws, L.z);
+  void *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *z = at(ws, L.z);
   float *gpart = (float *)at(ws, L.gpart);
 
-  SPA_TRY(launch_rmsnorm(D.dtype, h_in, idx, k_per_seq, D.N, M, D.d, w->g_attn, D.eps, a1, s));
-  SPA_TRY(mk.mark("rmsnorm_gather"));
-
+  // RMSNorm(g_attn) is fused into the QKV GEMM: it reads the raw rows of h_in gathered through idx
   EpiArgs qkv{};
   qkv.out = q;
   qkv.out2 = c->k_cache;
@@ -209,10 +204,12 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.dkv = D.dkv;
   qkv.hkv = D.hkv;
   qkv.hd = D.hd;
+  qkv.norm_d = D.d;
+  qkv.norm_eps = D.eps;
   const int nqkv = D.dq + 2 * D.dkv;
   const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);
-  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, a1, D.d, w->w_qkv, packed_wkb(D.dtype, D.d), M, nqkv, D.d, gpart, qkv,
-                      s));
+  SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, h_in, D.d, w->w_qkv, packed_wkb(D.dtype, D.d), M, nqkv, D.d, gpart,
+                      qkv, s));
   SPA_TRY(mk.mark("qkv_gemm_scatter", gemm_kernels(p_qkv)));
 
   SPA_TRY(launch_attention(D.dtype, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd, s));
@@ -231,14 +228,14 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
                       s));
   SPA_TRY(mk.mark("wo_gemm_residual", gemm_kernels(p_wo)));
 
-  SPA_TRY(launch_rmsnorm(D.dtype, y, nullptr, M, M, M, D.d, w->g_ffn, D.eps, b1, s));
-  SPA_TRY(mk.mark("rmsnorm"));
-
+  // RMSNorm(g_ffn) is fused into the gate/up GEMM, which reads y directly
   EpiArgs gu{};
   gu.out = z;
   gu.f = D.Fp;  // Z is M x F_pad; the zero-padded gate/up rows write zeros into the pad columns
+  gu.norm_d = D.d;
+  gu.norm_eps = D.eps;
   const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.Fp, D.d, kEpiSwiGLU);
-  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, b1, D.d, w->w_gate_up, packed_wkb(D.dtype, D.d), M, 2 * D.Fp, D.d,
+  SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, y, D.d, w->w_gate_up, packed_wkb(D.dtype, D.d), M, 2 * D.Fp, D.d,
                       gpart, gu, s));
   SPA_TRY(mk.mark("gate_up_gemm_swiglu", gemm_kernels(p_gu)));
 
@@ -312,15 +309,17 @@ int spa_packed_weight_bytes(int32_t dtype, int32_t rows, int32_t cols, int32_t k
   return SPA_OK;
 }
 
-int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src, void *dst,
-                    hipStream_t stream) {
+int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src,
+                    const void *col_scale, void *dst, hipStream_t stream) {
   size_t bytes = 0;
   const int st = spa_packed_weight_bytes(dtype, rows, cols, kind, &bytes);
   if (st != SPA_OK) return st;
   if (src == nullptr || dst == nullptr) return SPA_ERR_INVALID_ARG;
-  if (!aligned16(src) || !aligned16(dst)) return SPA_ERR_ALIGN;
-  if (overlap(src, (size_t)rows * cols * (dtype == SPA_BF16 ? 2 : 4), dst, bytes)) return SPA_ERR_ALIAS;
-  return hip_status(launch_pack_weight(dtype, kind, rows, cols, src, dst, stream));
+  if (!aligned16(src) || !aligned16(dst) || (col_scale != nullptr && !aligned16(col_scale))) return SPA_ERR_ALIGN;
+  const size_t e = dtype == SPA_BF16 ? 2 : 4;
+  if (overlap(src, (size_t)rows * cols * e, dst, bytes)) return SPA_ERR_ALIAS;
+  if (col_scale != nullptr && overlap(col_scale, (size_t)cols * e, dst, bytes)) return SPA_ERR_ALIAS;
+  return hip_status(launch_pack_weight(dtype, kind, rows, cols, src, col_scale, dst, stream));
 }
 
 int spa_workspace_bytes(const spa_shape *shape, int32_t k_max, size_t *bytes_out) {

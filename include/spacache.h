@@ -88,21 +88,25 @@ typedef enum { SPA_PACK_PLAIN = 0, SPA_PACK_GATE_UP = 1 } spa_pack_kind;
  * SPA_PACK_GATE_UP, where rows = 2F). */
 int spa_packed_weight_bytes(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, size_t *bytes_out);
 
-/* Pack a row-major device matrix into the fragment-packed layout (device, spa_packed_weight_bytes bytes,
- * must not overlap src). Stream-ordered; offline, once per model. */
-int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src, void *dst,
-                    hipStream_t stream);
+/* Pack a row-major device matrix src (rows x cols of dtype) into the fragment-packed layout (device,
+ * spa_packed_weight_bytes bytes, must not overlap src). col_scale (nullable; device, cols entries of
+ * dtype) packs W diag(col_scale) instead, the product taken in fp32 and rounded once to dtype: this is
+ * how an RMSNorm gain is folded into the weight that consumes the normalised rows. Stream-ordered;
+ * offline, once per model. */
+int spa_pack_weight(int32_t dtype, int32_t rows, int32_t cols, int32_t kind, const void *src,
+                    const void *col_scale, void *dst, hipStream_t stream);
 
 /* Layer weights (device, read-only). The block is pre-norm: RMSNorm(g_attn) -> QKV -> attention ->
- * W_o -> residual -> RMSNorm(g_ffn) -> SwiGLU -> W_down -> residual. Matrices are fragment-packed. */
+ * W_o -> residual -> RMSNorm(g_ffn) -> SwiGLU -> W_down -> residual. Matrices are fragment-packed.
+ * The two RMSNorm gains are folded into the matrices that follow them (spa_pack_weight's col_scale):
+ * since RMSNorm(x) W^T = (x W'^T) / rms(x) with W' = W diag(g), the library applies only the 1 / rms
+ * row scale, computed on the fly inside those GEMMs. */
 typedef struct {
   const void *w_r;        /* packed r x d: Lambda_r V_r^T of W_v diag(g_attn) ([PN] 关键设计 2)   */
-  const void *w_qkv;      /* packed (d_q + 2 d_kv) x d: rows [W_q; W_k; W_v]                      */
+  const void *w_qkv;      /* packed (d_q + 2 d_kv) x d: rows [W_q; W_k; W_v], col_scale g_attn     */
   const void *w_o;        /* packed d x d_q                                                       */
-  const void *w_gate_up;  /* packed SPA_PACK_GATE_UP of the 2F x d matrix [W_gate; W_up]          */
+  const void *w_gate_up;  /* packed SPA_PACK_GATE_UP of [W_gate; W_up] (2F x d), col_scale g_ffn  */
   const void *w_down;     /* packed d x F                                                         */
-  const void *g_attn;     /* d: attention RMSNorm gain (plain vector)                             */
-  const void *g_ffn;      /* d: FFN RMSNorm gain (plain vector)                                   */
 } spa_layer_weights;
 
 /* Per-layer caches (device, read-write), owned by the caller across steps. */

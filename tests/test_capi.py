@@ -109,7 +109,7 @@ def _fake(addr):
 
 def _weights(base=0x100000, misalign=None):
     from adaptive_hidden_state_amd import binding
-    vals = [base + 0x1000000 * i for i in range(7)]
+    vals = [base + 0x1000000 * i for i in range(5)]
     if misalign is not None:
         vals[misalign] += 2
     return binding.spa_layer_weights(*[_fake(v) for v in vals])
@@ -216,5 +216,8 @@ def test_packed_weight_bytes(lib):
     assert lib.spa_packed_weight_bytes(1, 101, 80, 1, ctypes.byref(out)) == -1          # odd gate/up rows
     assert lib.spa_packed_weight_bytes(5, 100, 80, 0, ctypes.byref(out)) == -2          # dtype
     assert lib.spa_packed_weight_bytes(1, 100, 80, 3, ctypes.byref(out)) == -1          # kind
-    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x1000 + 64), None) == -3
-    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1008), _fake(0x100000), None) == -4
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), None, _fake(0x1000 + 64), None) == -3
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1008), None, _fake(0x100000), None) == -4
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x200008), _fake(0x100000), None) == -4  # scale
+    assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x100040), _fake(0x100000), None) == -3  # scale
+    assert lib.spa_pack_weight(1, 64, 64, 0, None, None, _fake(0x100000), None) == -1

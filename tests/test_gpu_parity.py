@@ -90,9 +90,9 @@ def _check_step(case, k, policy=oracle.POLICY_ALL):
         I = i_g[b]
         rest = np.setdiff1d(np.arange(s.n_tokens), I)
         if k:
-            assert rel_l2(hh[b][I], ref.h[b][I]) <= tol, ("H", b, rel_l2(hh[b][I], ref.h[b][I]))
-            assert rel_l2(hk[b][:, I], ref.k[b][:, I]) <= tol, ("K", b)
-            assert rel_l2(hv[b][:, I], ref.v[b][:, I]) <= tol, ("V", b)
+            errs = {"H": rel_l2(hh[b][I], ref.h[b][I]), "K": rel_l2(hk[b][:, I], ref.k[b][:, I]),
+                    "V": rel_l2(hv[b][:, I], ref.v[b][:, I])}
+            assert max(errs.values()) <= tol, (b, errs)
         assert np.array_equal(hh[b][rest], case.cache0.h[b][rest])
         assert np.array_equal(hk[b][:, rest], case.cache0.k[b][:, rest])
         assert np.array_equal(hv[b][:, rest], case.cache0.v[b][:, rest])
@@ -343,14 +343,19 @@ def _pack_reference(w, kind, e):
     return np.concatenate(out)
 
 
+@pytest.mark.parametrize("scaled", [False, True])
 @pytest.mark.parametrize("dtype,rows,cols,kind", [("bf16", 200, 96, 0), ("bf16", 2 * 688, 256, 1),
                                                   ("f32", 16, 256, 0), ("f32", 2 * 48, 80, 1)])
-def test_pack_weight_layout_bit_exact(dtype, rows, cols, kind):
+def test_pack_weight_layout_bit_exact(dtype, rows, cols, kind, scaled):
     import torch
     spa = _lib()
     rng = np.random.default_rng(rows + cols)
     w = synth.to_storage(rng.standard_normal((rows, cols)), dtype)
-    packed = spa.spa_pack_weight(dev(w, dtype), kind)
+    g = synth.to_storage(rng.uniform(0.5, 1.5, cols), dtype) if scaled else None
+    packed = spa.spa_pack_weight(dev(w, dtype), kind, col_scale=None if g is None else dev(g, dtype))
     torch.cuda.synchronize()
-    ref = _pack_reference(w.astype(np.float32), kind, 2 if dtype == "bf16" else 4)
+    src = w.astype(np.float32)
+    if scaled:  # W diag(g): the product in fp32, rounded once to the storage type
+        src = synth.to_storage(src * g.astype(np.float32), dtype).astype(np.float32)
+    ref = _pack_reference(src, kind, 2 if dtype == "bf16" else 4)
     assert np.array_equal(packed.float().cpu().numpy(), ref)
