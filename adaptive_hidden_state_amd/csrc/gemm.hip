@@ -43,8 +43,36 @@ __device__ __forceinline__ void store8(float *p, const float *v) {
 
 // Epilogue of output row m, columns n0 .. n0 + 7 (n0 % 8 == 0; every width here is a multiple of 8,
 // and so is every head or hidden-unit boundary, so the eight never straddle one).
+template <typename T> __device__ __forceinline__ float stored_sq8(const float *r);
+template <> __device__ __forceinline__ float stored_sq8<float>(const float *r) {
+  float s = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) s = fmaf(r[x], r[x], s);
+  return s;
+}
+template <> __device__ __forceinline__ float stored_sq8<bf16_t>(const float *r) {  // of the bf16-rounded values
+  float s = 0.f;
+#pragma unroll
+  for (int x = 0; x < 8; x += 2) {
+    const uint32_t h = pack_bf16x2(r[x], r[x + 1]);
+    const float lo = __uint_as_float(h << 16), hi = __uint_as_float(h & 0xffff0000u);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+
+// Sum of squares of a row's 32-column block, kept by the first of the 4 consecutive lanes (or
+// threads) that handle its four 8-column chunks: every lane calls this (shuffles), valid or not.
+__device__ __forceinline__ void write_ss32(const EpiArgs &ea, int m, int n0, int N, float ss, bool valid,
+                                           bool first) {
+  ss += __shfl_xor(ss, 1, kWave);
+  ss += __shfl_xor(ss, 2, kWave);
+  if (valid && first) ea.ss_out[(size_t)m * (N / 32) + n0 / 32] = ss;
+}
+
 template <typename T, int KIND>
-__device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const float *v) {
+__device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const float *v, float *ssq = nullptr) {
   if constexpr (KIND == kEpiQKV) {
     if (n0 < ea.dq) {
       store8((T *)ea.out + (size_t)m * ea.dq + n0, v);
@@ -70,6 +98,7 @@ __device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const flo
 #pragma unroll
     for (int x = 0; x < 8; ++x) r[x] += v[x];
     store8((T *)ea.out + (size_t)m * ea.ldo + n0, r);
+    if (ssq != nullptr) *ssq = stored_sq8<T>(r);
   } else if constexpr (KIND == kEpiResidScatter) {
     int b;
     const int i = map_token(ea, m, b);
@@ -154,10 +183,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
     a_src[j] = reinterpret_cast<const char *>(A + gr * lda + k0) + col * 16;
     a_dst[j] = row * ROWB + col * 16;
   }
-  // fused RMSNorm: this thread's share (16 bytes per slab) of the sum of squares of its A rows
+  // Proxy projection over the hidden rows: this thread's share (16 bytes per slab) of the sum of
+  // squares of its A rows, for the RMSNorm fused into the QKV GEMM (one column tile writes it).
+  const bool acc_ss = KIND == kEpiPartial && ea.ss_out != nullptr && tn == 0;
   float ssq[A_PER];
 #pragma unroll
   for (int j = 0; j < A_PER; ++j) ssq[j] = 0.f;
+  // RMSNorm row scales of this tile, from the producers' statistics (computed after the first slabs'
+  // loads are issued, visible after the first barrier)
+  auto norm_scales = [&]() {
+    if (ea.row_rinv != nullptr) {
+      for (int r = tid; r < BM; r += 256) {
+        const int m = min(tm * BM + r, M - 1);
+        size_t src = (size_t)m;
+        if (ea.idx != nullptr) {
+          int b;
+          const int i = map_token(ea, m, b);
+          src = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+        }
+        row_scale[r] = ea.row_rinv[src];
+      }
+    } else {  // 256 / BM consecutive threads per row sum its partials (4 at a time) in a fixed order
+      constexpr int TPR = 256 / BM;
+      const int r = tid / TPR, part_i = tid % TPR;
+      const int m = min(tm * BM + r, M - 1);
+      const floatx4 *ps = reinterpret_cast<const floatx4 *>(ea.ss_in + (size_t)m * ea.ss_n);
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = part_i; j < ea.ss_n / 4; j += TPR) v += ps[j];
+      float t = (v[0] + v[1]) + (v[2] + v[3]);
+      if constexpr (TPR >= 2) t += __shfl_xor(t, 1, kWave);
+      if constexpr (TPR >= 4) t += __shfl_xor(t, 2, kWave);
+      if (part_i == 0) row_scale[r] = 1.0f / sqrtf(t / (float)ea.norm_d + ea.norm_eps);
+    }
+  };
   // B: this wave's column blocks, blocks 2 wk and 2 wk + 1 of every slab (four blocks per slab)
   const int cb0 = (tn * BN + wn * (BN / 2)) / 32;
   const int cb_last = (N + 31) / 32 - 1;
@@ -190,7 +249,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll
       for (int j = 0; j < A_PER; ++j) {
         st16(dst + a_dst[j], xa[j]);
-        if constexpr (NORM) {
+        if (acc_ss) {
           if constexpr (BF) {  // exact fp32 squares (bf16 -> fp32 is a shift), fp32 accumulation
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
@@ -222,8 +281,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
   if (nk > 0) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) gload(u, ra[u], rb[u]);
-    lstore(0, 0, ra[0]);
   }
+  if constexpr (NORM) norm_scales();
+  if (nk > 0) lstore(0, 0, ra[0]);
   __syncthreads();
 
   const int frag_off = (lane & 31) * ROWB + (lane >> 5) * LANE_B;
@@ -262,14 +322,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
     }
   }
 
-  if constexpr (NORM) {  // 8 consecutive lanes share a row; lane 0 of the 8 writes 1 / rms
+  if (acc_ss) {  // 8 consecutive lanes share a row; lane 0 of the 8 writes the split's sum of squares
 #pragma unroll
     for (int j = 0; j < A_PER; ++j) {
       float v = ssq[j];
       v += __shfl_xor(v, 1, kWave);
       v += __shfl_xor(v, 2, kWave);
       v += __shfl_xor(v, 4, kWave);
-      if ((tid & 7) == 0) row_scale[(tid + j * 256) >> 3] = 1.0f / sqrtf(v / (float)ea.norm_d + ea.norm_eps);
+      const int m = tm * BM + ((tid + j * 256) >> 3);
+      if ((tid & 7) == 0 && m < M) ea.ss_out[(size_t)split * M + m] = v;
     }
   }
 
@@ -350,7 +411,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
       }
     }
   } else {
-    for (int idx = lane; idx < ER * EC / 8; idx += 64) {
+    for (int idx = lane; idx < ER * EC / 8; idx += 64) {  // uniform trip count (ER EC / 8 % 64 == 0)
       const int lr = idx / (EC / 8), c8 = idx - lr * (EC / 8);
       const int m = mbase + lr, n0 = nbase + c8 * 8;
       if (m < M && n0 < N) {
@@ -360,9 +421,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll
           for (int x = 0; x < 8; ++x) v[x] = ep[lr * ES + c8 * 8 + x] * sc;
           epi8<T, KIND>(ea, m, n0, v);
-        } else {
+        } else if constexpr (KIND != kEpiResid) {
           epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
         }
+      }
+      if constexpr (KIND == kEpiResid) {  // EC / 8 is a multiple of 4: chunks c8 & ~3 .. | 3 share a block
+        float ss = 0.f;
+        const bool valid = m < M && n0 < N;
+        if (valid) epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8, &ss);
+        if (ea.ss_out != nullptr) write_ss32(ea, m, n0, N, ss, valid, (c8 & 3) == 0);
       }
     }
   }
@@ -394,16 +461,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     epi8_swiglu<T>(ea, m, j0, g, u);
   } else {
     const int n8 = N / 8;
-    if (t >= (size_t)M * n8) return;
-    const int m = (int)(t / n8), n0 = (int)(t - (size_t)m * n8) * 8;
-    float v[8] = {};
-    for (int s = 0; s < splits; ++s) {
-      float a[8];
-      load8(part + s * plane + (size_t)m * N + n0, a);
+    const bool valid = t < (size_t)M * n8;
+    const size_t tc = valid ? t : (size_t)M * n8 - 1;
+    const int m = (int)(tc / n8), n0 = (int)(tc - (size_t)m * n8) * 8;
+    float ss = 0.f;
+    if (valid) {
+      float v[8] = {};
+      for (int s = 0; s < splits; ++s) {
+        float a[8];
+        load8(part + s * plane + (size_t)m * N + n0, a);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) v[x] += a[x];
+        for (int x = 0; x < 8; ++x) v[x] += a[x];
+      }
+      epi8<T, KIND>(ea, m, n0, v, &ss);
     }
-    epi8<T, KIND>(ea, m, n0, v);
+    // N % 32 == 0, so threads t & ~3 .. t | 3 hold the four chunks of one 32-column block
+    if constexpr (KIND == kEpiResid)
+      if (ea.ss_out != nullptr) write_ss32(ea, m, n0, N, ss, valid, (t & 3) == 0);
   }
 }
 

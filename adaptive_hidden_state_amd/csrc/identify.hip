@@ -16,7 +16,9 @@ constexpr int kMaxSplits = 16;       // the proxy GEMM never splits K more than 
 
 __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
                                                            int r, const float *pc_read, float *pc_write,
-                                                           float *__restrict__ p_out, float *__restrict__ scores) {
+                                                           float *__restrict__ p_out, float *__restrict__ scores,
+                                                           const float *__restrict__ ss_part, int d, float eps,
+                                                           float *__restrict__ rinv) {
   // one wave per row, four consecutive columns per lane per chunk (16-byte accesses; r % 16 == 0)
   constexpr int kChunks = kMaxRankPerLane / 4;  // r <= 1024: 4 chunks of 64 lanes x 4 columns
   const int lane = threadIdx.x & 63;
@@ -51,6 +53,12 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
     }
     p[c] = v;
   }
+  // the row's 1 / rms for the RMSNorm fused into the QKV GEMM (split partials summed in order)
+  if (rinv != nullptr) {  // lane sp holds split sp's partial; a fixed reduction tree adds them
+    float ss = lane < splits ? ss_part[(size_t)lane * rows + row] : 0.f;
+    ss = wave_sum(ss);
+    if (lane == 0) rinv[row] = 1.0f / sqrtf(ss / (float)d + eps);
+  }
   if (pc_read != nullptr && scores != nullptr) {
     dot = wave_sum(dot);
     n1 = wave_sum(n1);
@@ -68,10 +76,38 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
 }
 
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read, float *pc_write,
-                               float *p_out, float *scores, hipStream_t s) {
+                               float *p_out, float *scores, const float *ss_part, int d, float eps, float *rinv,
+                               hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(proxy_cosine_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, part, splits, rows, r, pc_read,
-                     pc_write, p_out, scores);
+                     pc_write, p_out, scores, ss_part, d, eps, rinv);
+  return hipGetLastError();
+}
+
+// rinv[row] = 1 / sqrt(mean(x_row^2) + eps) over d columns; one wave per row (for the sparse update
+// called without the identification pass that otherwise produces these scales).
+template <typename T>
+__global__ __launch_bounds__(64) void row_rinv_kernel(const T *__restrict__ x, int d, float eps,
+                                                      float *__restrict__ rinv) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  const T *row = x + (size_t)blockIdx.x * d;
+  float ss = 0.f;
+  for (int v = threadIdx.x; v < d / VEC; v += 64) {
+    float f[VEC];
+    unpack16(ld16(row + v * VEC), f, row);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss = fmaf(f[e], f[e], ss);
+  }
+  ss = wave_sum(ss);
+  if (threadIdx.x == 0) rinv[blockIdx.x] = 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+hipError_t launch_row_rinv(int dtype, const void *x, int rows, int d, float eps, float *rinv, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(row_rinv_kernel<bf16_t>, dim3(rows), dim3(64), 0, s, (const bf16_t *)x, d, eps, rinv);
+  else
+    hipLaunchKernelGGL(row_rinv_kernel<float>, dim3(rows), dim3(64), 0, s, (const float *)x, d, eps, rinv);
   return hipGetLastError();
 }
 

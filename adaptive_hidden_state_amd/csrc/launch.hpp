@@ -34,9 +34,19 @@ struct EpiArgs {
   int f;
   // RMSNorm fused into the A operand (kinds kEpiQKV and kEpiSwiGLU): A rows are the raw hidden rows
   // (gathered through idx when it is set), the RMSNorm gain is folded into the packed weight, and
-  // each output row is scaled by 1 / sqrt(mean(a^2) + norm_eps) over the norm_d columns of A.
+  // each output row is scaled by 1 / sqrt(mean(a^2) + norm_eps) over the norm_d columns of A. The
+  // statistics come from the producers of A: row_rinv[source row] holds the scale itself (QKV: from
+  // the proxy GEMM over the same rows), or ss_in[m * ss_n + j], j < ss_n, holds partial sums of
+  // squares of row m (gate/up: from the W_o epilogue, one per 32 output columns).
   int norm_d;
   float norm_eps;
+  const float *row_rinv;
+  const float *ss_in;
+  int ss_n;
+  // Producer side: kEpiPartial with ss_out set also writes, for each A row, the sum of squares of its
+  // elements in the split's K range to ss_out[split * M + m]; kEpiResid with ss_out set writes the sum
+  // of squares of each row's stored outputs per 32 columns to ss_out[m * (N / 32) + n / 32].
+  float *ss_out;
 };
 
 struct GemmPlan {
@@ -85,8 +95,13 @@ hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const voi
                               void *dst, hipStream_t s);
 
 // Phase 1 pieces.
+// ss_part (splits x rows, nullable): the proxy GEMM's per-split sums of squares of each hidden row;
+// with rinv set, rinv[row] = 1 / sqrt(sum / d + eps) is written as well.
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,
-                               float *pc_write, float *p_out, float *scores, hipStream_t s);
+                               float *pc_write, float *p_out, float *scores, const float *ss_part, int d,
+                               float eps, float *rinv, hipStream_t s);
+// rinv[row] = 1 / sqrt(mean(x_row^2) + eps) for rows x d.
+hipError_t launch_row_rinv(int dtype, const void *x, int rows, int d, float eps, float *rinv, hipStream_t s);
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s);
 hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *idx, int batch, int n,
                                 int k, int r, hipStream_t s);

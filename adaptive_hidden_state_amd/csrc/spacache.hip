@@ -67,7 +67,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace regions. Offsets are multiples of 256 bytes.
 struct Layout {
   GemmPlan proxy;
-  size_t ppart, pbuf, scores, q, o, y, z, gpart, total;
+  size_t ppart, pbuf, scores, ssp, rinv, q, o, y, z, ss32, gpart, total;
 };
 
 Layout make_layout(const Dims &D, int k_max) {
@@ -84,10 +84,13 @@ Layout make_layout(const Dims &D, int k_max) {
   L.ppart = take(gemm_partial_bytes(L.proxy, (int)rows, D.r));
   L.pbuf = take(rows * D.r * 4);
   L.scores = take(rows * 4);
+  L.ssp = take((size_t)L.proxy.splits * rows * 4);  // per-split sums of squares of the hidden rows
+  L.rinv = take(rows * 4);                          // their 1 / rms (attention RMSNorm)
   L.q = take(m * D.dq * D.e);
   L.o = take(m * D.dq * D.e);
   L.y = take(m * D.d * D.e);
   L.z = take(m * D.Fp * D.e);
+  L.ss32 = take(m * (D.d / 32) * 4);  // sums of squares of y per 32 columns (FFN RMSNorm)
   // Split-K partials of the four k-row GEMMs: gemm_partial_bound(M, N) covers every plan with
   // M <= B * k_max rows.
   size_t gp = 0;
@@ -172,11 +175,14 @@ int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w
                  float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s, Marks &mk) {
   const int rows = D.B * D.N;
   float *part = (float *)at(ws, L.ppart);
+  float *ssp = (float *)at(ws, L.ssp), *rinv = (float *)at(ws, L.rinv);
   EpiArgs ea{};
+  ea.ss_out = ssp;  // the projection streams every hidden row: it also sums their squares
   SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, packed_wkb(D.dtype, D.d), rows, D.r, D.d, part,
                       ea, s));
   SPA_TRY(mk.mark("proxy_gemm"));
-  SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, s));
+  SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, ssp, D.d, D.eps,
+                              rinv, s));
   SPA_TRY(mk.mark("proxy_cosine"));
   return SPA_OK;
 }
@@ -184,13 +190,14 @@ int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w
 // number of kernels launch_gemm enqueues for a plan (the GEMM, plus the split-K reduce)
 int gemm_kernels(const GemmPlan &p) { return p.splits > 1 ? 2 : 1; }
 
-// Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N).
+// Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N). The 1 / rms
+// of every row of h_in must already be in the workspace (run_identify or launch_row_rinv).
 int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const spa_layer_cache *c,
                const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s, Marks &mk) {
   const int M = D.B * k_per_seq;
   if (M == 0) return SPA_OK;
   void *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *z = at(ws, L.z);
-  float *gpart = (float *)at(ws, L.gpart);
+  float *gpart = (float *)at(ws, L.gpart), *ss32 = (float *)at(ws, L.ss32);
 
   // RMSNorm(g_attn) is fused into the QKV GEMM: it reads the raw rows of h_in gathered through idx
   EpiArgs qkv{};
@@ -206,6 +213,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.hd = D.hd;
   qkv.norm_d = D.d;
   qkv.norm_eps = D.eps;
+  qkv.row_rinv = (const float *)at(ws, L.rinv);
   const int nqkv = D.dq + 2 * D.dkv;
   const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);
   SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, h_in, D.d, w->w_qkv, packed_wkb(D.dtype, D.d), M, nqkv, D.d, gpart,
@@ -223,6 +231,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   wo.n_tok = D.N;
   wo.ld_src = D.d;
   wo.ldo = D.d;
+  wo.ss_out = ss32;  // statistics of y for the FFN RMSNorm
   const GemmPlan p_wo = plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid);
   SPA_TRY(launch_gemm(D.dtype, kEpiResid, p_wo, o, D.dq, w->w_o, packed_wkb(D.dtype, D.dq), M, D.d, D.dq, gpart, wo,
                       s));
@@ -234,6 +243,8 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   gu.f = D.Fp;  // Z is M x F_pad; the zero-padded gate/up rows write zeros into the pad columns
   gu.norm_d = D.d;
   gu.norm_eps = D.eps;
+  gu.ss_in = ss32;
+  gu.ss_n = D.d / 32;
   const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.Fp, D.d, kEpiSwiGLU);
   SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, y, D.d, w->w_gate_up, packed_wkb(D.dtype, D.d), M, 2 * D.Fp, D.d,
                       gpart, gu, s));
@@ -432,6 +443,7 @@ int spa_sparse_update(const spa_shape *shape, const spa_layer_weights *w, const 
   const Layout L = make_layout(D, k);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
   Marks mk{nullptr, stream};
+  if (k > 0) SPA_TRY(launch_row_rinv(D.dtype, h_in, D.B * D.N, D.d, D.eps, (float *)at(ws, L.rinv), stream));
   return run_sparse(D, L, w, cache, h_in, idx, k, ws, stream, mk);
 }
 
