@@ -133,6 +133,23 @@ def summarize_profile(trace_csv=None, counter_csvs=()):
     return "\n".join(out)
 
 
+def kernel_work(name, s, k):
+    """Algorithmic bytes and flops of one kernel of the cached step (inputs read once, outputs written
+    once), for the per-kernel HBM / MFMA fractions."""
+    e = 2 if s.dtype == "bf16" else 4
+    rows, M = s.batch * s.n_tokens, s.batch * k
+    if name == "proxy_gemm":
+        return (rows * s.d_model + s.rank * s.d_model) * e + rows * s.rank * 4, 2.0 * rows * s.d_model * s.rank
+    if name == "proxy_cosine":
+        return rows * s.rank * 4 * 3 + rows * 4, 6.0 * rows * s.rank
+    if name == "topk":
+        return rows * 4 + M * 4, 0.0
+    if name == "attention":
+        kv = 2 * s.batch * s.n_kv_heads * s.n_tokens * s.head_dim * e
+        return kv + 2 * M * s.d_q * e, 4.0 * M * s.n_q_heads * s.n_tokens * s.head_dim
+    return gemm_work(name, s, M)
+
+
 def cpu_baseline(wl, w, w_r, xs, k, seconds):
     """The oracle's cached layer step timed on the host cores (bounded sample)."""
     import numpy as np
@@ -167,6 +184,9 @@ def main():
     ap.add_argument("--workload", default="llada-layer", choices=["llada-layer", "tiny-f32"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--instances", type=int, default=4,
+                    help="independent layer instances visited in turn (defeats Infinity-Cache reuse)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="time eager launches")
     ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--summarize-counters", metavar="CSV", nargs="*", default=[],
                     help="summarise rocprofv3 counter_collection.csv files and exit")
@@ -202,40 +222,79 @@ def main():
     xs, _ = synth.drift_sequence(wl)
     log(f"[bench] inputs ready in {time.time() - t:.1f} s")
 
-    dw = spa.upload_weights(w, w_r, s.dtype)
+    # R independent layer instances (weights, caches, inputs at distinct addresses), visited in turn, so
+    # that no step finds the previous step's data in the 256 MB Infinity Cache (one cycle streams > 1 GB)
+    R = max(1, args.instances)
+    dw0 = spa.upload_weights(w, w_r, s.dtype)
+    dws = [dw0] + [spa.DeviceWeights(*(t.clone() for t in dw0)) for _ in range(R - 1)]
     tdt = spa.torch_dtype(s.dtype)
-    xd = [torch.from_numpy(x).to("cuda", tdt).contiguous() for x in xs]
-    cache = spa.alloc_cache(s)
+    xd0 = [torch.from_numpy(x).to("cuda", tdt).contiguous() for x in xs]
+    xds = [xd0] + [[t.clone() for t in xd0] for _ in range(R - 1)]
+    caches = [spa.alloc_cache(s) for _ in range(R)]
     ws = spa.alloc_workspace(s, s.n_tokens)
     idx = torch.empty(s.batch, k, dtype=torch.int32, device="cuda")
     scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
-    n_in = len(xd) - 1
-
-    spa.spa_layer_full(s, dw, cache, xd[0], ws)
+    n_in = len(xd0) - 1
+    for r in range(R):
+        spa.spa_layer_full(s, dws[r], caches[r], xds[r][0], ws)
     torch.cuda.synchronize()
 
     # vanilla full recompute of the same layer (the "Baseline 100%" path), for the speedup
-    scratch = spa.alloc_cache(s)
-    for _ in range(2):
-        spa.spa_layer_full(s, dw, scratch, xd[1], ws)
+    scratch = [spa.alloc_cache(s) for _ in range(R)]
+    for r in range(R):
+        spa.spa_layer_full(s, dws[r], scratch[r], xds[r][1], ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_full = 10
+    n_full = 4 * R
     e0.record()
     for i in range(n_full):
-        spa.spa_layer_full(s, dw, scratch, xd[1 + i % n_in], ws)
+        spa.spa_layer_full(s, dws[i % R], scratch[i % R], xds[i % R][1 + (i // R) % n_in], ws)
     e1.record()
     torch.cuda.synchronize()
     ms_full = e0.elapsed_time(e1) / n_full
     del scratch
 
+    def which(i):  # step i -> (instance, input step)
+        return i % R, 1 + (i // R) % n_in
+
+    def eager_step(i):
+        r, j = which(i)
+        spa.spa_layer_step(s, dws[r], caches[r], xds[r][j], k, spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
+
+    # one captured HIP graph per (instance, input step); every launch of a step is stream-ordered and
+    # allocation-free, so the step is capturable as is
+    graphs = None
+    if args.graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for i in range(R * n_in):
+                    eager_step(i)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graphs = []
+            for i in range(R * n_in):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    eager_step(i)
+                graphs.append(g)
+            torch.cuda.synchronize()
+        except Exception as exc:  # fall back to eager launches
+            log(f"[bench] graph capture unavailable ({exc}); timing eager launches")
+            graphs = None
+
     def step(i):
-        spa.spa_layer_step(s, dw, cache, xd[1 + i % n_in], k, spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
+        if graphs is not None:
+            r, j = which(i)
+            graphs[r * n_in + (j - 1)].replay()
+        else:
+            eager_step(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} cached layer steps")
+    log(f"[bench] timing {args.steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances)")
     e0.record()
     for i in range(args.steps):
         step(args.warmup + i)
@@ -248,7 +307,8 @@ def main():
     per = {}
     n_prof = max(10, min(args.steps, 50))
     for i in range(n_prof):
-        res = spa.spa_layer_step_timed(s, dw, cache, xd[1 + i % n_in], k, spa.SPA_PROXY_WRITE_ALL, idx, scores,
+        r, j = which(i)
+        res = spa.spa_layer_step_timed(s, dws[r], caches[r], xds[r][j], k, spa.SPA_PROXY_WRITE_ALL, idx, scores,
                                        ws, ev)
         seen = {}
         for name, ms in res:
@@ -258,11 +318,22 @@ def main():
     ev.close()
     per_us = {n: 1000.0 * float(np.median(v)) for n, v in per.items()}
 
+    peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
+    per_kernel = {}
+    for n, us in per_us.items():
+        wk = kernel_work(n, s, k)
+        if wk is None:
+            continue
+        byts, flops = wk
+        per_kernel[n] = {"us": round(us, 2), "GB/s": round(byts / us / 1e3, 1),
+                         "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
+                         "TFLOP/s": round(flops / us / 1e6, 1),
+                         "mfma_frac": round(flops / us / 1e6 / peak_flops, 4)}
+
     # roofline of the dominant kernel
     dom = max((n for n in per_us if gemm_work(n, s, M)), key=lambda n: per_us[n])
     byts, flops = gemm_work(dom, s, M)
     dur_s = per_us[dom] * 1e-6
-    peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
     hbm_bound = byts / (PEAK_HBM_GBS * 1e9) >= flops / (peak_flops * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": byts / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -296,6 +367,9 @@ def main():
         "full_recompute_ms": round(ms_full, 5),
         "speedup_vs_full": round(ms_full / ms_step, 3),
         "per_kernel_us": {n: round(v, 2) for n, v in per_us.items()},
+        "per_kernel_roofline": per_kernel,
+        "timing": {"graphs": graphs is not None, "instances": R,
+                   "note": "per-kernel us from HIP events recorded between kernels on the launch stream"},
         "roofline": roof,
         "gpu": torch.cuda.get_device_name(0),
     }
