@@ -24,7 +24,16 @@ def singular_proxy_from_factors(lam, v_right, r: int, g_attn=None) -> np.ndarray
 
     Valid only when the gain is 1 everywhere (then W_v diag(g) = W_v and its factors are known).
     """
-    if g_attn is not None and not np.all(np.asarray(g_attn) == 1):
-        raise ValueError("closed-form factors need unit RMSNorm gains; use singular_proxy_weights")
+    def is_torch(a):
+        return type(a).__module__.startswith("torch")
+
+    if g_attn is not None:
+        ones = bool((g_attn == 1).all()) if is_torch(g_attn) else bool(np.all(np.asarray(g_attn) == 1))
+        if not ones:
+            raise ValueError("closed-form factors need unit RMSNorm gains; use singular_proxy_weights")
+    if is_torch(v_right):  # torch tensor (device-side factors of the large workloads)
+        import torch
+        lam_t = torch.as_tensor(np.asarray(lam[:r], dtype=np.float64), dtype=torch.float64, device=v_right.device)
+        return lam_t[:, None] * v_right[:r].to(torch.float64)
     lam = np.asarray(lam, dtype=np.float64)
     return lam[:r, None] * np.asarray(v_right, dtype=np.float64)[:r]

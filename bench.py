@@ -176,44 +176,96 @@ def cpu_baseline(wl, w, w_r, xs, k, seconds):
                       f"k={k}) by the NumPy float64 oracle, {el:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llada-layer", choices=["llada-layer", "tiny-f32"])
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--instances", type=int, default=4,
-                    help="independent layer instances visited in turn (defeats Infinity-Cache reuse)")
-    ap.add_argument("--no-graph", dest="graph", action="store_false", help="time eager launches")
-    ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")
-    ap.add_argument("--summarize-counters", metavar="CSV", nargs="*", default=[],
-                    help="summarise rocprofv3 counter_collection.csv files and exit")
-    args = ap.parse_args()
-    if args.summarize_trace or args.summarize_counters:
-        print(summarize_profile(args.summarize_trace, args.summarize_counters))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
+def roofline_of(byts, flops, us, peak_flops):
+    """Roofline record of one kernel: its nearer bound (HBM bytes or MFMA flops) and the fraction."""
+    dur_s = us * 1e-6
+    if byts / (PEAK_HBM_GBS * 1e9) >= flops / (peak_flops * 1e12):
+        roof = {"bound": "hbm", "achieved": byts / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / dur_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    return roof
 
+
+def per_kernel_fractions(per_us, work, peak_flops):
+    out = {}
+    for n, us in per_us.items():
+        if n not in work:
+            continue
+        byts, flops = work[n]
+        out[n] = {"us": round(us, 2), "GB/s": round(byts / us / 1e3, 1),
+                  "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
+                  "TFLOP/s": round(flops / us / 1e6, 1), "mfma_frac": round(flops / us / 1e6 / peak_flops, 4)}
+    return out
+
+
+def dominant_roofline(per_us, work, peak_flops, workload):
+    """Roofline of the longest GEMM (the dominant kernel of every workload here)."""
+    dom = max((n for n in per_us if n in work and n in GEMM_KERNELS), key=lambda n: per_us[n])
+    byts, flops = work[dom]
+    roof = roofline_of(byts, flops, per_us[dom], peak_flops)
+    roof["traffic"] = measured_traffic(dom, workload)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = byts
+    roof["algorithmic_flops"] = flops
+    roof["mfma_frac"] = flops / (per_us[dom] * 1e-6) / 1e12 / peak_flops
+    return roof
+
+
+def ideal_floor_us(work, peak_flops):
+    """Sum over kernels of max(bytes / HBM peak, flops / MFMA peak): no schedule can beat it."""
+    return sum(max(b / (PEAK_HBM_GBS * 1e3), f / (peak_flops * 1e6)) for b, f in work.values())
+
+
+GEMM_KERNELS = ("qkv_gemm_scatter", "wo_gemm_residual", "gate_up_gemm_swiglu", "down_gemm_scatter")
+STEP_KERNELS = ("proxy_gemm", "proxy_cosine", "topk") + GEMM_KERNELS[:1] + ("attention",) + GEMM_KERNELS[1:]
+
+
+def base_line(args, wl, s, value, unit, ms_step, steps, warmup, data):
+    return {
+        "metric": "tokens/s & layer-steps/s (8B-shape, N=1024, r=128) + % HBM/MFMA peak",
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": data,
+    }
+
+
+def timed_kernels(spa, calls, reps):
+    """Per-kernel durations (us, median over reps) of a sequence of spa_layer_step_timed calls;
+    `calls(ev)` runs one pass and returns [(name, ms), ...] summed over its layers."""
+    import numpy as np
+    ev = spa.HipEvents(24)
+    per = {}
+    for _ in range(reps):
+        tot = {}
+        for name, ms in calls(ev):
+            tot[name] = tot.get(name, 0.0) + ms
+        for name, ms in tot.items():
+            per.setdefault(name, []).append(ms)
+    ev.close()
+    return {n: 1000.0 * float(np.median(v)) for n, v in per.items()}
+
+
+def run_layer(args, wl):
+    """One layer of a workload, cached steps over rotating layer instances, graph-replayed."""
     import numpy as np
     import torch
 
     import adaptive_hidden_state_amd as spa
     import synth
 
-    if not torch.cuda.is_available():
-        log("no GPU visible")
-        sys.exit(1)
-    spa.load_library()
-    torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
     s = wl.shape
     k = int(spa.spa_budget(1, 1, wl.rho, wl.rho, wl.rho, s.n_tokens)[1][0])
-    M = s.batch * k
+    steps = args.steps or 200
+    warmup = 10 if args.warmup is None else args.warmup
 
     log(f"[bench] generating {wl.name} weights and inputs")
     t = time.time()
@@ -263,26 +315,7 @@ def main():
 
     # one captured HIP graph per (instance, input step); every launch of a step is stream-ordered and
     # allocation-free, so the step is capturable as is
-    graphs = None
-    if args.graph:
-        try:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for i in range(R * n_in):
-                    eager_step(i)
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            graphs = []
-            for i in range(R * n_in):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    eager_step(i)
-                graphs.append(g)
-            torch.cuda.synchronize()
-        except Exception as exc:  # fall back to eager launches
-            log(f"[bench] graph capture unavailable ({exc}); timing eager launches")
-            graphs = None
+    graphs = capture(args, [lambda i=i: eager_step(i) for i in range(R * n_in)]) if args.graph else None
 
     def step(i):
         if graphs is not None:
@@ -291,95 +324,454 @@ def main():
         else:
             eager_step(i)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances)")
+    log(f"[bench] timing {steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances)")
     e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(steps):
+        step(warmup + i)
     e1.record()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = e0.elapsed_time(e1) / steps
 
     # per-kernel durations: HIP events between the kernels of the same step sequence
-    ev = spa.HipEvents(24)
-    per = {}
-    n_prof = max(10, min(args.steps, 50))
-    for i in range(n_prof):
-        r, j = which(i)
-        res = spa.spa_layer_step_timed(s, dws[r], caches[r], xds[r][j], k, spa.SPA_PROXY_WRITE_ALL, idx, scores,
-                                       ws, ev)
-        seen = {}
-        for name, ms in res:
-            seen[name] = seen.get(name, 0.0) + ms
-        for name, ms in seen.items():
-            per.setdefault(name, []).append(ms)
-    ev.close()
-    per_us = {n: 1000.0 * float(np.median(v)) for n, v in per.items()}
+    it = iter(range(10 ** 9))
 
+    def one(ev):
+        r, j = which(next(it))
+        return spa.spa_layer_step_timed(s, dws[r], caches[r], xds[r][j], k, spa.SPA_PROXY_WRITE_ALL, idx, scores,
+                                        ws, ev)
+
+    per_us = timed_kernels(spa, one, max(10, min(steps, 50)))
     peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
-    per_kernel = {}
-    for n, us in per_us.items():
-        wk = kernel_work(n, s, k)
-        if wk is None:
-            continue
-        byts, flops = wk
-        per_kernel[n] = {"us": round(us, 2), "GB/s": round(byts / us / 1e3, 1),
-                         "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4),
-                         "TFLOP/s": round(flops / us / 1e6, 1),
-                         "mfma_frac": round(flops / us / 1e6 / peak_flops, 4)}
+    work = {n: kernel_work(n, s, k) for n in STEP_KERNELS}
 
-    # roofline of the dominant kernel
-    dom = max((n for n in per_us if gemm_work(n, s, M)), key=lambda n: per_us[n])
-    byts, flops = gemm_work(dom, s, M)
-    dur_s = per_us[dom] * 1e-6
-    hbm_bound = byts / (PEAK_HBM_GBS * 1e9) >= flops / (peak_flops * 1e12)
-    if hbm_bound:
-        roof = {"bound": "hbm", "achieved": byts / dur_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": flops / dur_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom, wl.name)
-    roof["kernel"] = dom
-    roof["algorithmic_bytes"] = byts
-    roof["algorithmic_flops"] = flops
-    roof["mfma_frac"] = flops / dur_s / 1e12 / peak_flops
-
-    value = s.batch / (ms_step * 1e-3)
-    line = {
-        "metric": "tokens/s & layer-steps/s (8B-shape, N=1024, r=128) + % HBM/MFMA peak",
-        "value": round(value, 2),
-        "unit": "layer-steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": s.dtype,
-        "data": "synthetic (seeded random-init weights with a planted Value spectrum; drifting N(0,1) hidden states)",
-        "config": {"workload": wl.name, "batch": s.batch, "n_tokens": s.n_tokens, "d_model": s.d_model,
-                   "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
-                   "d_ffn": s.d_ffn, "rank": s.rank, "rho": wl.rho, "k": k},
-        "tokens_per_s_projected": round(16 * s.batch / (32 * ms_step * 1e-3), 2),
-        "full_recompute_ms": round(ms_full, 5),
-        "speedup_vs_full": round(ms_full / ms_step, 3),
-        "per_kernel_us": {n: round(v, 2) for n, v in per_us.items()},
-        "per_kernel_roofline": per_kernel,
-        "timing": {"graphs": graphs is not None, "instances": R,
-                   "note": "per-kernel us from HIP events recorded between kernels on the launch stream"},
-        "roofline": roof,
-        "gpu": torch.cuda.get_device_name(0),
-    }
+    line = base_line(args, wl, s, s.batch / (ms_step * 1e-3), "layer-steps/s", ms_step, steps, warmup,
+                     "synthetic (seeded random-init weights with a planted Value spectrum; drifting N(0,1) "
+                     "hidden states)")
+    line["config"] = {"workload": wl.name, "batch": s.batch, "n_tokens": s.n_tokens, "d_model": s.d_model,
+                      "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                      "d_ffn": s.d_ffn, "rank": s.rank, "rho": wl.rho, "k": k}
+    line["tokens_per_s_projected"] = round(16 * s.batch / (32 * ms_step * 1e-3), 2)
+    line["full_recompute_ms"] = round(ms_full, 5)
+    line["speedup_vs_full"] = round(ms_full / ms_step, 3)
+    line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
+    line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
+    line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
+    line["timing"] = {"graphs": graphs is not None, "instances": R,
+                      "note": "per-kernel us from HIP events recorded between kernels on the launch stream"}
+    line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["gpu"] = torch.cuda.get_device_name(0)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        import oracle  # noqa: F401  (test infrastructure, only for this baseline leg)
-        w_r64 = np.asarray(w_r, np.float64)
-        line["cpu_baseline"] = cpu_baseline(wl, w, w_r64, xs, k, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, w, np.asarray(w_r, np.float64), xs, k, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
+    return line
+
+
+def capture(args, fns):
+    """One captured HIP graph per callable (each a stream-ordered, allocation-free sequence of library
+    calls), after one eager pass of all of them on a side stream; None if capture is unavailable."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for f in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+    except Exception as exc:  # fall back to eager launches
+        log(f"[bench] graph capture unavailable ({exc}); timing eager launches")
+        return None
+
+
+def host_weights(w):
+    """float32 host copies of a device weight dict (inputs of the CPU oracle baseline)."""
+    import numpy as np
+    return {key: (v.float().cpu().numpy() if hasattr(v, "device") else np.asarray(v))
+            for key, v in w.items() if key.startswith(("w_", "g_"))}
+
+
+def run_stack(args, wl):
+    """A multi-layer stack: every denoising step unmasks u tokens (fresh embedding rows at their
+    positions of the layer-0 input) and runs the cached step of every layer, layer l reading layer
+    l-1's output cache; k_l from the piecewise-Gaussian budget (or its mean, uniform)."""
+    import numpy as np
+    import torch
+
+    import adaptive_hidden_state_amd as spa
+    import synth
+
+    s = wl.shape
+    if args.identifier == "full":
+        s = s.replace(rank=s.d_kv)
+    elif args.rank:
+        s = s.replace(rank=args.rank)
+    L, u, B, N = wl.n_layers, wl.unmask_per_step, s.batch, s.n_tokens
+    rho_p, l_p, rho_1, rho_L = wl.budget
+    rhos, ks = spa.spa_budget(L, l_p, rho_p, rho_1, rho_L, N)
+    if args.budget == "uniform":
+        mean = float(np.mean(rhos))
+        ks = spa.spa_budget(1, 1, mean, mean, mean, N)[1] * L
+    steps = args.steps or wl.steps
+    warmup = 4 if args.warmup is None else args.warmup
+    tdt = spa.torch_dtype(s.dtype)
+
+    log(f"[bench] generating {L} {wl.name} layers on the device")
+    t0 = time.time()
+    pair = synth.haar_pair(wl, s)
+    layers = []
+    for l in range(L):
+        w = synth.layer_weights_device(wl, l + 1, pair, shape=s)
+        if args.identifier == "full":   # the full-dimension Value identifier: W_r = W_v diag(g_attn) = W_v
+            w_r = w["w_v"]
+        else:
+            w_r = spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], s.rank, w["g_attn"]).to(tdt)
+        layers.append(spa.upload_weights(w, w_r, s.dtype))
+        del w, w_r
+    torch.cuda.synchronize()
+    pos, rows = synth.unmask_schedule(wl, s)
+    rows_neg = -rows
+    x0 = synth.normal_device((B, N, s.d_model), wl.config_id, 0, synth.STREAM_X0, dtype=s.dtype)
+    x_buf = x0.clone()
+    caches = [spa.alloc_cache(s) for _ in range(L)]
+    ws = spa.alloc_workspace(s, N)
+    idx = torch.empty(B, max(ks), dtype=torch.int32, device="cuda")
+    scores = torch.empty(B, N, dtype=torch.float32, device="cuda")
+    t_sched = pos.shape[0]
+    log(f"[bench] {L} layers ready in {time.time() - t0:.1f} s; k_l = {ks}")
+
+    def feed(t):  # unmask the step's u positions (every second pass over the schedule flips the rows' sign)
+        c, j = divmod(t, t_sched)
+        x_buf.index_copy_(1, pos[j], rows[j] if c % 2 == 0 else rows_neg[j])
+
+    def chain(full):
+        x = x_buf
+        for l in range(L):
+            if full:
+                spa.spa_layer_full(s, layers[l], caches[l], x, ws)
+            else:
+                spa.spa_layer_step(s, layers[l], caches[l], x, ks[l], spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
+            x = caches[l].h
+
+    chain(True)  # warm-up at step 0 (every layer fully computed)
+    torch.cuda.synchronize()
+    graphs = capture(args, [lambda: chain(False)]) if args.graph else None
+
+    def step(t):
+        feed(t)
+        if graphs is not None:
+            graphs[0].replay()
+        else:
+            chain(False)
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {steps} denoising steps x {L} layers ({'graph' if graphs else 'eager'})")
+    e0.record()
+    for t in range(steps):
+        step(warmup + t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+
+    def one(ev):
+        feed(warmup + steps)
+        x, res = x_buf, []
+        for l in range(L):
+            res += spa.spa_layer_step_timed(s, layers[l], caches[l], x, ks[l], spa.SPA_PROXY_WRITE_ALL, idx,
+                                            scores, ws, ev)
+            x = caches[l].h
+        return res
+
+    per_us = timed_kernels(spa, one, 3)
+    peak_flops = PEAK_BF16_TFLOPS
+    work = {}
+    for n in STEP_KERNELS:
+        b = f = 0.0
+        for kl in ks:
+            bb, ff = kernel_work(n, s, kl)
+            b, f = b + bb, f + ff
+        work[n] = (b, f)
+
+    # vanilla decoding: every layer fully recomputed at every step
+    n_full = max(2, min(steps, 8))
+    e0.record()
+    for t in range(n_full):
+        feed(warmup + steps + 1 + t)
+        chain(True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_full = e0.elapsed_time(e1) / n_full
+
+    line = base_line(args, wl, s, u * B / (ms_step * 1e-3), "tokens/s", ms_step, steps, warmup,
+                     "synthetic (seeded random-init layers with a planted Value spectrum, drawn on the device; "
+                     "N(0,1) embeddings, u fresh rows per denoising step; layers chained)")
+    line["config"] = {"workload": wl.name, "n_layers": L, "batch": B, "n_tokens": N, "d_model": s.d_model,
+                      "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
+                      "d_ffn": s.d_ffn, "rank": s.rank, "identifier": args.identifier, "budget": args.budget,
+                      "rho_peak_lpeak_first_last": list(wl.budget), "k_per_layer": ks,
+                      "mean_k": round(float(np.mean(ks)), 2), "unmask_per_step": u}
+    line["layer_steps_per_s"] = round(L * B / (ms_step * 1e-3), 2)
+    line["full_recompute_ms"] = round(ms_full, 5)
+    line["speedup_vs_full"] = round(ms_full / ms_step, 3)
+    line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
+    line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
+    line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
+    line["timing"] = {"graphs": graphs is not None, "instances": 1,
+                      "note": "ms_per_step = one denoising step through all layers (the unmasking copy "
+                              "included); per-kernel us summed over the layers of one step"}
+    line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["gpu"] = torch.cuda.get_device_name(0)
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline_sample(wl, s, pair, ks, [0, l_p - 1, L - 1], x0, pos, rows,
+                                                   args.cpu_seconds, args.identifier)
+    return line
+
+
+def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, identifier):
+    """The oracle's cached step on a sample of one stack's layers (each with its own k_l), from the
+    step-0 embeddings and the first unmasking step, within a bounded time."""
+    import numpy as np
+    import oracle
+    import adaptive_hidden_state_amd as spa
+    import synth
+    threads = blas_threads()
+    x0h = x0.float().cpu().numpy().astype(np.float64)
+    x1 = x0.clone()
+    x1.index_copy_(1, pos[0], rows[0])
+    x1h = x1.float().cpu().numpy().astype(np.float64)
+    done, el = 0, 0.0
+    for l in sample_layers:
+        w = synth.layer_weights_device(wl, l + 1, pair, shape=s)
+        if identifier == "full":
+            w_r = w["w_v"].float().cpu().numpy().astype(np.float64)
+        else:
+            w_r = spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], s.rank, w["g_attn"])
+            w_r = synth.to_storage(w_r.cpu().numpy(), s.dtype).astype(np.float64)
+        wh = host_weights(w)
+        del w
+        kc, vc = oracle.kv_project(x0h, wh, s.head_dim, s.norm_eps, s.dtype)
+        pc = oracle.proxy(x0h, w_r).astype(np.float32).astype(np.float64)
+        cache = oracle.LayerCache(kc, vc, x0h.copy(), pc)
+        t0 = time.perf_counter()
+        oracle.cached_layer_step(x1h, wh, w_r, cache, ks[l], s.head_dim, s.norm_eps, s.dtype)
+        el += time.perf_counter() - t0
+        done += 1
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "layer-steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one cached step of layers {[l + 1 for l in sample_layers[:done]]} of {wl.name} "
+                      f"(k = {[ks[l] for l in sample_layers[:done]]}, B={s.batch}, N={s.n_tokens}, d={s.d_model}) "
+                      f"by the NumPy float64 oracle, {el:.1f} s"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def run_batched(args, wl):
+    """The batched stress workload: one layer of the llada shape at B sequences of N tokens, over a
+    sweep of proxy ranks and budgets; rho = 1 also times the vanilla full recompute."""
+    import numpy as np
+    import torch
+
+    import adaptive_hidden_state_amd as spa
+    import synth
+
+    s0 = wl.shape
+    B, N = s0.batch, s0.n_tokens
+    ranks = args.ranks or [64, 128, 512]
+    rhos = [0.08, 0.16, 0.25, 1.0]
+    steps = args.steps or wl.steps
+    warmup = 2 if args.warmup is None else args.warmup
+    tdt = spa.torch_dtype(s0.dtype)
+
+    log(f"[bench] generating {wl.name} weights and {wl.steps} drift steps on the device")
+    pair = synth.haar_pair(wl, s0)
+    w = synth.layer_weights_device(wl, 0, pair, shape=s0)
+    base = spa.upload_weights(w, spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], s0.rank,
+                                                                 w["g_attn"]).to(tdt), s0.dtype)
+    w_rs = {r: spa.spa_pack_weight(spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], r,
+                                                                   w["g_attn"]).to(tdt).contiguous())
+            for r in ranks}
+    wh = host_weights(w) if not args.no_cpu_baseline else None
+    v_lam, v_right = w["v_lambda"], w["v_right"]
+    del w
+    xs = synth.drift_sequence_device(wl, s0)
+    n_in = len(xs) - 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sweep, head = [], None
+    peak_flops = PEAK_BF16_TFLOPS
+    for r in ranks:
+        s = s0.replace(rank=r)
+        dw = base._replace(w_r=w_rs[r])
+        cache = spa.alloc_cache(s)
+        ws = spa.alloc_workspace(s, N)
+        scores = torch.empty(B, N, dtype=torch.float32, device="cuda")
+        for rho in rhos:
+            k = int(spa.spa_budget(1, 1, rho, rho, rho, N)[1][0])
+            idx = torch.empty(B, k, dtype=torch.int32, device="cuda")
+            spa.spa_layer_full(s, dw, cache, xs[0], ws)
+
+            def step(i):
+                spa.spa_layer_step(s, dw, cache, xs[1 + i % n_in], k, spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
+
+            for i in range(warmup):
+                step(i)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(steps):
+                step(warmup + i)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            work = {n: kernel_work(n, s, k) for n in STEP_KERNELS}
+            floor = ideal_floor_us(work, peak_flops) / 1e3
+            pt = {"rank": r, "rho": rho, "k": k, "ms_per_step": round(ms, 4),
+                  "layer_steps_per_s": round(B / (ms * 1e-3), 2), "ideal_floor_ms": round(floor, 4),
+                  "floor_frac": round(floor / ms, 4)}
+            if rho == 1.0:
+                e0.record()
+                for i in range(steps):
+                    spa.spa_layer_full(s, dw, cache, xs[1 + i % n_in], ws)
+                e1.record()
+                torch.cuda.synchronize()
+                pt["full_recompute_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+            log(f"[bench] {pt}")
+            sweep.append(pt)
+            if r == s0.rank and rho == wl.rho:
+                it = iter(range(10 ** 9))
+
+                def one(ev):
+                    return spa.spa_layer_step_timed(s, dw, cache, xs[1 + next(it) % n_in], k,
+                                                    spa.SPA_PROXY_WRITE_ALL, idx, scores, ws, ev)
+
+                per_us = timed_kernels(spa, one, 5)
+                head = (ms, k, per_us, work)
+        del cache, ws
+    ms_step, k, per_us, work = head
+    full = {p["rank"]: p["full_recompute_ms"] for p in sweep if p["rho"] == 1.0}
+    line = base_line(args, wl, s0, B / (ms_step * 1e-3), "layer-steps/s", ms_step, steps, warmup,
+                     "synthetic (seeded random-init layer with a planted Value spectrum, drawn on the device; "
+                     "N(0,1) hidden states, 15% drifting rows per sequence and step)")
+    line["config"] = {"workload": wl.name, "batch": B, "n_tokens": N, "d_model": s0.d_model,
+                      "n_q_heads": s0.n_q_heads, "n_kv_heads": s0.n_kv_heads, "head_dim": s0.head_dim,
+                      "d_ffn": s0.d_ffn, "rank": s0.rank, "rho": wl.rho, "k": k,
+                      "sweep": {"rank": ranks, "rho": rhos}}
+    line["full_recompute_ms"] = full.get(s0.rank)
+    line["speedup_vs_full"] = round(full[s0.rank] / ms_step, 3) if s0.rank in full else None
+    line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
+    line["sweep"] = sweep
+    line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
+    line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
+    line["timing"] = {"graphs": False, "instances": 1,
+                      "note": "eager launches (steps of milliseconds); per-kernel us at the headline point"}
+    line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["gpu"] = torch.cuda.get_device_name(0)
+    line["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one sequence")
+        line["cpu_baseline"] = cpu_baseline_sequence(wl, s0, wh, v_lam, v_right, xs, args.cpu_seconds)
+    return line
+
+
+def cpu_baseline_sequence(wl, s0, wh, v_lam, v_right, xs, seconds):
+    """The oracle's cached step of one sequence of the batched workload (rank and rho of the
+    headline point), within a bounded time."""
+    import numpy as np
+    import oracle
+    import adaptive_hidden_state_amd as spa
+    import synth
+    s = s0.replace(batch=1)
+    k = int(spa.spa_budget(1, 1, wl.rho, wl.rho, wl.rho, s.n_tokens)[1][0])
+    w_r = synth.to_storage(spa.singular_proxy_from_factors(v_lam, v_right, s.rank, None).cpu().numpy(),
+                           s.dtype).astype(np.float64)
+    x = [xs[j][:1].float().cpu().numpy().astype(np.float64) for j in range(len(xs))]
+    kc, vc = oracle.kv_project(x[0], wh, s.head_dim, s.norm_eps, s.dtype)
+    pc = oracle.proxy(x[0], w_r).astype(np.float32).astype(np.float64)
+    cache = oracle.LayerCache(kc, vc, x[0].copy(), pc)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        cache, _, _ = oracle.cached_layer_step(x[1 + done % (len(x) - 1)], wh, w_r, cache, k, s.head_dim,
+                                               s.norm_eps, s.dtype)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "layer-steps/s", "cores": int(blas_threads()), "kind": "oracle",
+            "sample": f"{done} cached steps of one sequence of {wl.name} (N={s.n_tokens}, d={s.d_model}, "
+                      f"r={s.rank}, k={k}) by the NumPy float64 oracle, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 layer steps; the schedule's denoising steps for a stack; "
+                         "16 for the batched sweep)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="llada-layer",
+                    choices=["llada-layer", "tiny-f32", "llada-stack", "dream-stack", "batched-stress"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--instances", type=int, default=4,
+                    help="independent layer instances visited in turn (defeats Infinity-Cache reuse)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false", help="time eager launches")
+    ap.add_argument("--budget", choices=["adaptive", "uniform"], default="adaptive",
+                    help="stacks: piecewise-Gaussian rho(l), or its mean on every layer")
+    ap.add_argument("--rank", type=int, default=None, help="stacks: proxy rank r")
+    ap.add_argument("--identifier", choices=["proxy", "full"], default="proxy",
+                    help="stacks: singular proxy, or the full Value projection (r = d_kv)")
+    ap.add_argument("--ranks", type=int, nargs="*", default=None, help="batched sweep: proxy ranks")
+    ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV", nargs="*", default=[],
+                    help="summarise rocprofv3 counter_collection.csv files and exit")
+    args = ap.parse_args()
+    if args.summarize_trace or args.summarize_counters:
+        print(summarize_profile(args.summarize_trace, args.summarize_counters))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import adaptive_hidden_state_amd as spa
+    import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    spa.load_library()
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    if wl.n_layers > 1:
+        line = run_stack(args, wl)
+    elif wl.name == "batched-stress":
+        line = run_batched(args, wl)
+    else:
+        line = run_layer(args, wl)
     print(json.dumps(line), flush=True)
 
 

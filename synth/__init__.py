@@ -232,3 +232,110 @@ def random_weights(shape: LayerShape, seed: int, std: float = 0.02, spectrum: st
         w["g_attn"] = to_storage(rng.uniform(0.5, 1.5, shape.d_model).astype(np.float32), shape.dtype)
         w["g_ffn"] = to_storage(rng.uniform(0.5, 1.5, shape.d_model).astype(np.float32), shape.dtype)
     return w
+
+
+# ---------------------------------------------------------------------------------------------
+# Device-side generation for the multi-layer and batched workloads. A 32-layer stack holds ~13 GB
+# of weights, too much to draw with NumPy on the host in a benchmark's set-up, so these draw the
+# same distributions with a seeded torch generator on the device. Values differ from the NumPy
+# streams above (different generator); shapes, distributions and seeds-by-(config, layer, stream)
+# are the same. The planted Value projection reuses one host-drawn Haar pair per shape and gives
+# every layer its own signed row permutation of it, which keeps the columns orthonormal and the
+# planted spectrum exact while avoiding a 4096 x 4096 QR per layer.
+# ---------------------------------------------------------------------------------------------
+
+def _torch_gen(config_id: int, layer: int, stream: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(config_id) * 1_000_003 + int(layer) * 1009 + int(stream))
+    return g
+
+
+def haar_pair(wl: Workload, shape: Optional[LayerShape] = None):
+    """Host-drawn orthonormal factors (U: d_kv x n, V: d x n, n = min(d_kv, d)) shared by a workload's
+    layers, plus the planted singular values (float64)."""
+    s = shape or wl.shape
+    hr = _rng(wl.config_id, 0, STREAM_HAAR)
+    n = min(s.d_kv, s.d_model)
+    return _haar(hr, s.d_kv, n), _haar(hr, s.d_model, n), planted_spectrum(wl.spectrum, n, s.d_kv, s.d_model)
+
+
+def layer_weights_device(wl: Workload, layer: int, pair, device="cuda", shape: Optional[LayerShape] = None,
+                         std: float = 0.02) -> Dict[str, object]:
+    """Random-init weights of one layer as device tensors in the storage dtype ([out][in] row-major),
+    drawn on the device. w_v = (S P U) diag(lambda) (S' P' V)^T with this layer's random row
+    permutations P, P' and sign flips S, S' of the shared Haar pair; "v_lambda" (host float64) and
+    "v_right" (device float32, n x d: rows are the right singular vectors) are returned too."""
+    import torch
+    s = shape or wl.shape
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    g = _torch_gen(wl.config_id, layer, STREAM_WEIGHTS, device)
+    d, dq, dkv, f = s.d_model, s.d_q, s.d_kv, s.d_ffn
+
+    def normal(rows, cols):
+        return (torch.randn(rows, cols, generator=g, device=device, dtype=torch.float32) * std).to(tdt)
+
+    w = {"w_q": normal(dq, d), "w_k": normal(dkv, d), "w_o": normal(d, dq), "w_gate": normal(f, d),
+         "w_up": normal(f, d), "w_down": normal(d, f)}
+    u0, v0, lam = pair
+    gh = _torch_gen(wl.config_id, layer, STREAM_HAAR, device)
+
+    def signed_perm(m):
+        rows = torch.randperm(m.shape[0], generator=gh, device=device)
+        sign = torch.randint(0, 2, (m.shape[0], 1), generator=gh, device=device).to(torch.float32) * 2 - 1
+        return m[rows] * sign
+
+    u = signed_perm(torch.as_tensor(u0, dtype=torch.float32, device=device))
+    v = signed_perm(torch.as_tensor(v0, dtype=torch.float32, device=device))
+    lam_t = torch.as_tensor(lam, dtype=torch.float32, device=device)
+    w["w_v"] = ((u * lam_t[None, :]) @ v.T).to(tdt)
+    w["v_lambda"] = np.asarray(lam, dtype=np.float64)
+    w["v_right"] = v.T.contiguous()
+    w["g_attn"] = torch.ones(d, dtype=tdt, device=device)
+    w["g_ffn"] = torch.ones(d, dtype=tdt, device=device)
+    return w
+
+
+def normal_device(shape: tuple, config_id: int, layer: int, stream: int, device="cuda", std: float = 1.0,
+                  dtype: str = "bf16"):
+    """A seeded N(0, std^2) device tensor rounded to the storage dtype (inputs of the large workloads)."""
+    import torch
+    g = _torch_gen(config_id, layer, stream, device)
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32) * std
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def unmask_schedule(wl: Workload, shape: Optional[LayerShape] = None, device="cuda"):
+    """Denoising schedule of a stack workload: T = N / u steps, step t unmasks the u positions
+    perm[t u : (t + 1) u] of one seeded permutation of the N positions, and gives them fresh N(0, 1)
+    embedding rows. Returns (positions T x u int64, rows T x B x u x d in the storage dtype)."""
+    import torch
+    s = shape or wl.shape
+    u = wl.unmask_per_step
+    t_steps = s.n_tokens // u
+    g = _torch_gen(wl.config_id, 0, STREAM_DRIFT, device)
+    perm = torch.randperm(s.n_tokens, generator=g, device=device)[: t_steps * u].reshape(t_steps, u)
+    rows = normal_device((t_steps, s.batch, u, s.d_model), wl.config_id, 1, STREAM_DRIFT, device, 1.0, s.dtype)
+    return perm.contiguous(), rows
+
+
+def drift_sequence_device(wl: Workload, shape: Optional[LayerShape] = None, n_steps: Optional[int] = None,
+                          device="cuda"):
+    """Device analogue of drift_sequence for the batched workload: X^0 ~ N(0, 1); at every step each
+    sequence gets N(0, 0.5^2) on round(f N) random rows and N(0, (1e-3)^2) elsewhere, re-rounded to
+    the storage dtype."""
+    import torch
+    s = shape or wl.shape
+    steps = wl.steps if n_steps is None else n_steps
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    xs = [normal_device((s.batch, s.n_tokens, s.d_model), wl.config_id, 0, STREAM_X0, device, 1.0, s.dtype)]
+    g = _torch_gen(wl.config_id, 0, STREAM_DRIFT, device)
+    n_drift = int(round(wl.drift_frac * s.n_tokens))
+    for _ in range(steps):
+        noise = torch.randn(s.batch, s.n_tokens, s.d_model, generator=g, device=device) * 1e-3
+        for b in range(s.batch):
+            rows = torch.randperm(s.n_tokens, generator=g, device=device)[:n_drift]
+            noise[b, rows] = torch.randn(n_drift, s.d_model, generator=g, device=device) * 0.5
+        xs.append((xs[-1].to(torch.float32) + noise).to(tdt))
+        del noise
+    return xs
