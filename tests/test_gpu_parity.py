@@ -52,51 +52,60 @@ class Case:
         return w, c
 
 
-def _check_step(case, k, policy=oracle.POLICY_ALL):
+def _slice(cache, sel):
+    return oracle.LayerCache(cache.k[sel], cache.v[sel], cache.h[sel], cache.p[sel])
+
+
+def _check_step(case, k, policy=oracle.POLICY_ALL, seqs=None):
+    """One cached step on the GPU against the oracle. Scores, the proxy cache and the untouched rows
+    are checked for every sequence; block outputs for the sequences in `seqs` (default: all). The
+    oracle only ever sees host inputs: when the GPU's set differs from the oracle's by near-ties,
+    the GPU's phases 2-3 are re-run on the oracle's set (spa_sparse_update) and compared with that."""
     import torch
     spa = _lib()
     s = case.shape
+    sel = list(range(s.batch)) if seqs is None else list(seqs)
     w, c = case.device()
     x1 = dev(case.x1, s.dtype)
     idx = torch.empty(s.batch, k, dtype=torch.int32, device="cuda")
     scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
-    ws = spa.alloc_workspace(s, k)
+    ws = spa.alloc_workspace(s, max(k, 1))
     spa.spa_layer_step(s, w, c, x1, k, policy, idx, scores, ws)
     torch.cuda.synchronize()
 
-    new_o, idx_o, s_o = oracle.cached_layer_step(case.x1, case.w, case.w_r, case.cache0, k, s.head_dim, EPS,
-                                                 s.dtype, policy)
+    p_new, s_o = oracle.identify(case.x1, case.w_r, case.cache0.p)
+    idx_o = np.stack([oracle.select_topk(s_o[b], k) for b in range(s.batch)]) if k else np.zeros((s.batch, 0), int)
     s_g = host(scores)
     assert np.max(np.abs(s_g - s_o)) <= 1e-3
     i_g = host(idx).astype(np.int64)
-    ref = new_o
+    same = True
     for b in range(s.batch):
-        if k:
-            ndiff = check_near_ties(i_g[b], idx_o[b], s_o[b], k)
-            if ndiff:
-                ref = None
-    if ref is None:   # near-tie swaps: recompute the oracle's phases 2-3 on the GPU's sets
-        ref = oracle.sparse_update(case.x1, case.w, case.cache0, i_g, s.head_dim, EPS, s.dtype)
-        if policy == oracle.POLICY_ALL:
-            ref.p = oracle.proxy(case.x1, case.w_r).astype(np.float32).astype(np.float64)
-        else:
-            ref.p = case.cache0.p.copy()
-            p_new = oracle.proxy(case.x1, case.w_r).astype(np.float32).astype(np.float64)
-            for b in range(s.batch):
-                ref.p[b][i_g[b]] = p_new[b][i_g[b]]
-    tol = tol_for(s.dtype)
+        if k and check_near_ties(i_g[b], idx_o[b], s_o[b], k):
+            same = same and b not in sel
     hk, hv, hh, hp = host(c.k), host(c.v), host(c.h), host(c.p)
+    # proxy cache: every row (ALL) or the rows of the step's set (SELECTED) take the new proxy
     for b in range(s.batch):
-        I = i_g[b]
-        rest = np.setdiff1d(np.arange(s.n_tokens), I)
-        if k:
-            errs = {"H": rel_l2(hh[b][I], ref.h[b][I]), "K": rel_l2(hk[b][:, I], ref.k[b][:, I]),
-                    "V": rel_l2(hv[b][:, I], ref.v[b][:, I])}
-            assert max(errs.values()) <= tol, (b, errs)
+        take = np.ones(s.n_tokens, bool) if policy == oracle.POLICY_ALL else np.isin(np.arange(s.n_tokens), i_g[b])
+        exp_p = np.where(take[:, None], p_new[b], case.cache0.p[b])
+        assert rel_l2(hp[b], exp_p) <= 1e-5, b
+        rest = np.setdiff1d(np.arange(s.n_tokens), i_g[b])
         assert np.array_equal(hh[b][rest], case.cache0.h[b][rest])
         assert np.array_equal(hk[b][:, rest], case.cache0.k[b][:, rest])
         assert np.array_equal(hv[b][:, rest], case.cache0.v[b][:, rest])
-    assert rel_l2(hp, ref.p) <= 1e-5
+    if not k:
+        return i_g, s_g
+    if not same:   # near-tie swaps in a checked sequence: the GPU's phases 2-3 on the oracle's set
+        w, c = case.device()
+        spa.spa_sparse_update(s, w, c, x1, torch.from_numpy(idx_o.astype(np.int32)).cuda(), ws)
+        torch.cuda.synchronize()
+        hk, hv, hh = host(c.k), host(c.v), host(c.h)
+    ref = oracle.sparse_update(case.x1[sel], case.w, _slice(case.cache0, sel), idx_o[sel], s.head_dim, EPS, s.dtype)
+    tol = tol_for(s.dtype)
+    for j, b in enumerate(sel):
+        I = idx_o[b]
+        errs = {"H": rel_l2(hh[b][I], ref.h[j][I]), "K": rel_l2(hk[b][:, I], ref.k[j][:, I]),
+                "V": rel_l2(hv[b][:, I], ref.v[j][:, I])}
+        assert max(errs.values()) <= tol, (b, errs)
     return i_g, s_g
 
 
@@ -303,6 +312,29 @@ def test_dream_layer_step_full_size():
     pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
     case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
     _check_step(case, int(ks[9]))          # layer 10 = the peak: k = 512
+
+
+@pytest.mark.timeout(900)
+def test_batched_stress_full_size_sampled():
+    """The batched stress layer at full size (B=8, N=4096, d=4096, r=128, rho=0.25 -> k=1024): every
+    sequence's scores, proxy cache, index set (near-ties) and untouched rows; the block outputs of the
+    first and the last sequence against the oracle."""
+    wl = synth.WORKLOADS["batched-stress"]
+    s = wl.shape
+    k = int(oracle.budget(1, 1, wl.rho, wl.rho, wl.rho, s.n_tokens)[1][0])
+    assert k == 1024
+    case = Case.__new__(Case)
+    case.shape = s
+    case.w = synth.layer_weights(wl)
+    case.w_r = synth.to_storage(oracle.singular_proxy(case.w["w_v"], case.w["g_attn"], s.rank), s.dtype)
+    xs, drifted = synth.drift_sequence(wl, n_steps=1)
+    case.x0, case.x1, case.drifted = xs[0], xs[1], drifted[0]
+    kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
+    pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
+    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
+    i_g, _ = _check_step(case, k, seqs=[0, s.batch - 1])
+    for b in range(s.batch):   # the 614 drifted tokens of every sequence are all selected
+        assert set(case.drifted[b].tolist()) <= set(i_g[b].tolist())
 
 
 def _pack_reference(w, kind, e):
