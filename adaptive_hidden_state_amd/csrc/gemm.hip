@@ -435,6 +435,272 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Large-M GEMM (bf16, M in the hundreds to thousands): 256 x 256 output tiles. At this M the weight
+// panel is reused by many row tiles, so the kernel is bound by MFMA issue and by the L2 -> CU
+// traffic per flop, which a 256 x 256 tile halves against 128 x 192. Both operands are copied from
+// global memory straight into LDS (global_load_lds, 16 bytes per lane, no registers and no LDS
+// store instructions on the way) through a ring of four 32-k slab stages, three in flight while one
+// is consumed. A sits in LDS row-major, 64 bytes per row, its 16-byte chunks XOR-swizzled by bits
+// 1..2 of the row so that both the copy (four lanes per row) and the MFMA fragment reads (32 rows
+// of one chunk) are free of bank conflicts; the packed weight blocks are copied as they are. Each
+// of the four waves owns a 128 x 128 quarter of the tile (16 accumulator blocks, 256 registers).
+// ---------------------------------------------------------------------------------------------
+struct BigLds {
+  static constexpr int kStage = 32 * 1024;                // A 16 KB + B 16 KB of one 32-k slab
+  static constexpr int kStages = 4;
+  static constexpr int kStride = 132;                     // staged output row (floats)
+  static constexpr int kEpi = 4 * 64 * kStride * 4;       // each wave's 64 x 128 half tile
+  static constexpr int kBytes = kEpi > kStages * kStage ? kEpi : kStages * kStage;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void global_void_t;
+
+// 16 bytes per lane from global memory into LDS at l + 16 lane (l uniform across the wave).
+__device__ __forceinline__ void copy_to_lds(const void *g, char *l) {
+  __builtin_amdgcn_global_load_lds((global_void_t *)g, (lds_void_t *)l, 16, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Eight 16-byte LDS reads (four at a + 2048 i, four at b + 1024 (2 j + S)) in one block that also
+// waits for them, so the results are complete when the block ends. The compiler does not see these
+// reads as LDS accesses and so adds no wait for copies in flight into other stages; the caller
+// orders them after the stage's copies (explicit wait and barrier).
+template <int S>
+__device__ __forceinline__ void lds_frags(const char *a, const char *b, u32x4 (&af)[4], u32x4 (&bf)[4]) {
+  const uint32_t va = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)a;
+  const uint32_t vb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)b;
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\t"
+      "ds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %9 offset:%10\n\t"
+      "ds_read_b128 %5, %9 offset:%11\n\t"
+      "ds_read_b128 %6, %9 offset:%12\n\t"
+      "ds_read_b128 %7, %9 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+      : "v"(va), "v"(vb), "i"(S * 1024), "i"((2 + S) * 1024), "i"((4 + S) * 1024), "i"((6 + S) * 1024)
+      : "memory");
+}
+
+// Per-thread copy plan of one slab: 4 A instructions (16 rows x 64 bytes each) and 4 weight-block
+// instructions (1 KB each) per wave.
+struct BigCopy {
+  const char *a_src[4];  // this lane's source 16 bytes of each A instruction, at slab 0
+  const char *b_src[2];  // this lane's 16 bytes of the wave's two weight column blocks, at slab 0
+  int wave;
+  int nk;
+};
+
+// The main loop, with the four stage buffers as distinct restrict pointers: the compiler can then
+// tell the fragment reads of one stage from the copies in flight into the others and needs no wait
+// for them; the copies a stage's reads depend on are waited for explicitly (each wave its own,
+// then a barrier).
+__device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__restrict__ s1, char *__restrict__ s2,
+                                              char *__restrict__ s3, const BigCopy &cp, int wm, int wn, int lane,
+                                              floatx16 (&acc)[4][4]) {
+  const int nk = cp.nk;
+  // fragment offsets: A row wm 128 + 32 i + lane % 32, logical chunk 2 s + lane / 32 (swizzled);
+  // weight block (wn 4 + j, k-step s)
+  const int arow = wm * 128 + (lane & 31), sw = ((lane & 31) >> 1) & 3;
+  const int a_off0 = arow * 64 + ((0 + (lane >> 5)) ^ sw) * 16;
+  const int a_off1 = arow * 64 + ((2 + (lane >> 5)) ^ sw) * 16;
+  const int b_off = 16384 + (wn * 8) * 1024 + lane * 16;
+  const int dst_a = cp.wave * 4 * 1024, dst_b = 16384 + cp.wave * 4 * 1024;
+
+// Slab KT (clamped) into stage DST.
+#define SPA_BIG_ISSUE(KT, DST)                                                                         \
+  do {                                                                                                 \
+    const int kc_ = min((KT), nk - 1);                                                                 \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
+        copy_to_lds(cp.a_src[j] + (size_t)kc_ * 64, (DST) + dst_a + j * 1024);                        \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
+        copy_to_lds(cp.b_src[j >> 1] + ((size_t)kc_ * 2 + (j & 1)) * 1024, (DST) + dst_b + j * 1024);  \
+  } while (0)
+// Slab KT from stage CUR after this wave's copies of it landed (slabs KT + 1, KT + 2 may stay in
+// flight) and every wave passed the barrier; slab KT + 3 into stage NXT, which every wave finished
+// reading before the barrier.
+#define SPA_BIG_STEP(KT, CUR, NXT)                                                                     \
+  do {                                                                                                 \
+    wait_vmem<16>();                                                                                   \
+    __builtin_amdgcn_s_barrier();                                                                      \
+    SPA_BIG_ISSUE((KT) + 3, NXT);                                                                      \
+    {                                                                                                  \
+      u32x4 af[4], bf[4];                                                                              \
+      lds_frags<0>((CUR) + a_off0, (CUR) + b_off, af, bf);                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
+      lds_frags<1>((CUR) + a_off1, (CUR) + b_off, af, bf);                                             \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
+    }                                                                                                  \
+  } while (0)
+
+  SPA_BIG_ISSUE(0, s0);
+  SPA_BIG_ISSUE(1, s1);
+  SPA_BIG_ISSUE(2, s2);
+  for (int kt = 0; kt < nk; kt += 4) {
+    SPA_BIG_STEP(kt, s0, s3);
+    if (kt + 1 < nk) SPA_BIG_STEP(kt + 1, s1, s0);
+    if (kt + 2 < nk) SPA_BIG_STEP(kt + 2, s2, s1);
+    if (kt + 3 < nk) SPA_BIG_STEP(kt + 3, s3, s2);
+  }
+#undef SPA_BIG_STEP
+#undef SPA_BIG_ISSUE
+  wait_vmem<0>();  // no copy may land in LDS after this point
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict__ A, int lda,
+                                                       const char *__restrict__ W, int wkb, int M, int N, int K,
+                                                       int tiles_m, int tiles_n, EpiArgs ea) {
+  typedef bf16_t T;
+  constexpr int BM = 256, BN = 256;
+  constexpr int STAGE = BigLds::kStage, ES = BigLds::kStride;
+  constexpr bool NORM = KIND == kEpiQKV || KIND == kEpiSwiGLU;
+  __shared__ __attribute__((aligned(1024))) char lds[BigLds::kBytes];
+  __shared__ float row_scale[NORM ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-contiguous ranges of the launch order (as the small-M kernel), and within the order groups
+  // of 8 row tiles: a group's A panels and the weight panel they share are read close together.
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int group = bid / (GM * tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int in_g = bid - group * GM * tiles_n;
+  const int tm = first_m + in_g % gsize;
+  const int tn = in_g / gsize;
+
+  // copy plan: A instruction j of a wave covers rows r0 .. r0 + 15 (r0 = 16 (4 wave + j)); lane l
+  // lands at LDS byte 16 l of it, i.e. row r0 + l / 4, physical chunk l % 4, and so fetches logical
+  // chunk (l % 4) ^ ((row >> 1) & 3) of that row. Weight instruction j copies block 4 wave + j of the
+  // slab (column block 2 wave + j / 2, k-step j % 2).
+  BigCopy cp;
+  cp.wave = wave;
+  cp.nk = K / 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 16 + (lane >> 2);
+    const int m = min(tm * BM + row, M - 1);
+    size_t gr = (size_t)m;
+    if (NORM && ea.idx != nullptr) {  // A rows gathered through the update set
+      int b;
+      const int i = map_token(ea, m, b);
+      gr = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+    }
+    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    cp.a_src[j] = reinterpret_cast<const char *>(A + gr * lda) + chunk * 16;
+  }
+  const int cb_last = (N + 31) / 32 - 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cb = min(tn * 8 + 2 * wave + h, cb_last);
+    cp.b_src[h] = W + (size_t)cb * wkb * 1024 + lane * 16;
+  }
+
+  auto norm_scales = [&]() {
+    if (ea.row_rinv != nullptr) {
+      const int m = min(tm * BM + tid, M - 1);
+      size_t src = (size_t)m;
+      if (ea.idx != nullptr) {
+        int b;
+        const int i = map_token(ea, m, b);
+        src = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+      }
+      row_scale[tid] = ea.row_rinv[src];
+    } else {  // one thread per row sums its partials (4 at a time) in a fixed order
+      const int m = min(tm * BM + tid, M - 1);
+      const floatx4 *ps = reinterpret_cast<const floatx4 *>(ea.ss_in + (size_t)m * ea.ss_n);
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = 0; j < ea.ss_n / 4; ++j) v += ps[j];
+      const float t = (v[0] + v[1]) + (v[2] + v[3]);
+      row_scale[tid] = 1.0f / sqrtf(t / (float)ea.norm_d + ea.norm_eps);
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  if constexpr (NORM) norm_scales();  // visible after the loop's barriers (and the one below)
+  if (cp.nk > 0) big_main_loop(lds, lds + STAGE, lds + 2 * STAGE, lds + 3 * STAGE, cp, wm, wn, lane, acc);
+  __syncthreads();
+
+  // Epilogue in two halves of 64 rows per wave: stage row-major in the wave's own LDS region (the
+  // wave reads back only what it wrote), then every lane finishes eight consecutive columns of a row.
+  constexpr int ER = 64, EC = 128;
+  float *ep = reinterpret_cast<float *>(lds) + wave * ER * ES;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          ep[(ii * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3)) * ES + j * 32 + (lane & 31)] = acc[2 * h + ii][j][q];
+    const int rbase = wm * 128 + h * 64;  // row of the tile
+    const int mbase = tm * BM + rbase, nbase = tn * BN + wn * EC;
+    if constexpr (KIND == kEpiSwiGLU) {
+      for (int idx = lane; idx < ER * EC / 16; idx += 64) {
+        const int lr = idx / (EC / 16), g8 = idx - lr * (EC / 16);
+        const int c = g8 >> 1, hh = g8 & 1;
+        const int m = mbase + lr, j0 = (nbase / 32 + c) * 16 + hh * 8;
+        const float *row = ep + lr * ES + c * 32 + hh * 8;
+        if (m < M && j0 < ea.f) {
+          float g[8], u[8];
+          const float sc = row_scale[rbase + lr];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            g[x] = row[x] * sc;
+            u[x] = row[16 + x] * sc;
+          }
+          epi8_swiglu<T>(ea, m, j0, g, u);
+        }
+      }
+    } else {
+      for (int idx = lane; idx < ER * EC / 8; idx += 64) {  // uniform trip count
+        const int lr = idx / (EC / 8), c8 = idx - lr * (EC / 8);
+        const int m = mbase + lr, n0 = nbase + c8 * 8;
+        if constexpr (KIND == kEpiResid) {  // chunks c8 & ~3 .. c8 | 3 share a 32-column block
+          float ss = 0.f;
+          const bool valid = m < M && n0 < N;
+          if (valid) epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8, &ss);
+          if (ea.ss_out != nullptr) write_ss32(ea, m, n0, N, ss, valid, (c8 & 3) == 0);
+        } else if (m < M && n0 < N) {
+          if constexpr (NORM) {
+            float v[8];
+            const float sc = row_scale[rbase + lr];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = ep[lr * ES + c8 * 8 + x] * sc;
+            epi8<T, KIND>(ea, m, n0, v);
+          } else {
+            epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order (deterministic), then the epilogue, eight columns (or
 // eight hidden units) per thread.
 template <typename T, int KIND>
@@ -539,6 +805,19 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       }
     }
   }
+  // The 256 x 256 kernel (bf16, no split): one 32-k slab per ~70 clocks when its tiles fit in one
+  // round, ~75 under full load (measured over M = 256 .. 8192, N = 3584 .. 37888); it wins once the
+  // tiles fill the chip.
+  if (dtype == kBF16 && kind != kEpiPartial) {
+    const long long tiles = (long long)ceil_div(M, 256) * ceil_div(N, 256);
+    const double cost = (double)ceil_div_ll(tiles, kCUs) * K * (tiles <= kCUs ? 70.0 : 75.0);
+    if (cost < best_cost) {
+      best.cfg = kBigTileCfg;
+      best.bm = best.bn = 256;
+      best.splits = 1;
+      best.k_split = K;
+    }
+  }
   best.tiles_m = ceil_div(M, best.bm);
   best.tiles_n = ceil_div(N, best.bn);
   return best;
@@ -576,6 +855,13 @@ static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void 
       case 2: return run_gemm<T, 128, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
       case 3: return run_gemm<T, 128, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
       case 4: return run_gemm<T, 64, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case kBigTileCfg:
+        if constexpr (KIND != kEpiPartial) {
+          hipLaunchKernelGGL(gemm_big_kernel<KIND>, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256), 0, s,
+                             (const bf16_t *)A, lda, (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, ea);
+          return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
       default: return run_gemm<T, 64, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
     }
   }

@@ -57,6 +57,9 @@ struct GemmPlan {
   int k_split;   // K elements per split (multiple of the K slab)
 };
 
+// Tile configuration of the large-M kernel: bf16 only, 256 x 256 tiles, never split, no kEpiPartial.
+constexpr int kBigTileCfg = 6;
+
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
 

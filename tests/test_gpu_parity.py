@@ -315,6 +315,27 @@ def test_dream_layer_step_full_size():
 
 
 @pytest.mark.timeout(900)
+def test_dream_layer_full_recompute_full_size():
+    """The full recompute (warm-up) of a Dream layer at full size (N=2048, GQA 28/4, F=18944): the
+    gate/up product then runs on 2048 rows, where the 256 x 256 GEMM tiles are used."""
+    import torch
+    spa = _lib()
+    wl = synth.WORKLOADS["dream-stack"]
+    s = wl.shape
+    w = synth.layer_weights(wl, layer=3)
+    w_r = synth.to_storage(oracle.singular_proxy(w["w_v"], w["g_attn"], s.rank), s.dtype)
+    x = synth.first_hidden(wl, layer=3)
+    dw = spa.upload_weights(w, w_r, s.dtype)
+    c = spa.alloc_cache(s)
+    ws = spa.alloc_workspace(s, s.n_tokens)
+    spa.spa_layer_full(s, dw, c, dev(x, s.dtype), ws)
+    torch.cuda.synchronize()
+    ref = oracle.warmup(x, w, w_r, s.head_dim, EPS, s.dtype)
+    errs = {"K": rel_l2(host(c.k), ref.k), "V": rel_l2(host(c.v), ref.v), "H": rel_l2(host(c.h), ref.h)}
+    assert max(errs.values()) <= 2e-2, errs
+    assert rel_l2(host(c.p), ref.p) <= 1e-5
+
+@pytest.mark.timeout(900)
 def test_batched_stress_full_size_sampled():
     """The batched stress layer at full size (B=8, N=4096, d=4096, r=128, rho=0.25 -> k=1024): every
     sequence's scores, proxy cache, index set (near-ties) and untouched rows; the block outputs of the
