@@ -11,47 +11,37 @@ namespace spa {
 // ---------------------------------------------------------------------------------------------
 // partial-sum reduce + cosine + proxy-cache write; one wave per token row
 // ---------------------------------------------------------------------------------------------
-constexpr int kMaxRankPerLane = 16;  // r <= 1024
-constexpr int kMaxSplits = 16;       // the proxy GEMM never splits K more than this
-
+// Reduce the proxy GEMM's split-K partials (in split order: deterministic), take the cosine against
+// the cached proxy, write the new proxy. One wave per row, streaming the row in chunks of 64 lanes x 4
+// columns (16-byte accesses; r % 16 == 0), so any rank works, up to the full Value width. Each lane
+// reads its columns of the cached proxy before it writes the same columns, so the cache may be
+// updated in place (pc_write == pc_read).
 __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
                                                            int r, const float *pc_read, float *pc_write,
                                                            float *__restrict__ p_out, float *__restrict__ scores,
                                                            const float *__restrict__ ss_part, int d, float eps,
                                                            float *__restrict__ rinv) {
-  // one wave per row, four consecutive columns per lane per chunk (16-byte accesses; r % 16 == 0)
-  constexpr int kChunks = kMaxRankPerLane / 4;  // r <= 1024: 4 chunks of 64 lanes x 4 columns
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const size_t plane = (size_t)rows * r;
   const size_t base = (size_t)row * r;
-  floatx4 p[kChunks];
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
+  for (int col = lane * 4; col < r; col += 256) {
+    floatx4 v = *reinterpret_cast<const floatx4 *>(part + base + col);
+    for (int sp = 1; sp < splits; ++sp) v += *reinterpret_cast<const floatx4 *>(part + sp * plane + base + col);
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int col = (lane + 64 * c) * 4;
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (col < r) {
-      floatx4 ps[kMaxSplits];
+    for (int x = 0; x < 4; ++x) n1 += v[x] * v[x];
+    if (pc_read != nullptr) {
+      const floatx4 w = *reinterpret_cast<const floatx4 *>(pc_read + base + col);
 #pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp)
-        ps[sp] = sp < splits ? *reinterpret_cast<const floatx4 *>(part + sp * plane + base + col)
-                             : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int sp = 0; sp < kMaxSplits; ++sp) v += ps[sp];  // fixed split order: deterministic
-#pragma unroll
-      for (int x = 0; x < 4; ++x) n1 += v[x] * v[x];
-      if (pc_read != nullptr) {
-        const floatx4 w = *reinterpret_cast<const floatx4 *>(pc_read + base + col);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          dot += v[x] * w[x];
-          n2 += w[x] * w[x];
-        }
+      for (int x = 0; x < 4; ++x) {
+        dot += v[x] * w[x];
+        n2 += w[x] * w[x];
       }
     }
-    p[c] = v;
+    if (p_out != nullptr) *reinterpret_cast<floatx4 *>(p_out + base + col) = v;
+    if (pc_write != nullptr) *reinterpret_cast<floatx4 *>(pc_write + base + col) = v;
   }
   // the row's 1 / rms for the RMSNorm fused into the QKV GEMM (split partials summed in order)
   if (rinv != nullptr) {  // lane sp holds split sp's partial; a fixed reduction tree adds them
@@ -64,14 +54,6 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
     n1 = wave_sum(n1);
     n2 = wave_sum(n2);
     if (lane == 0) scores[row] = dot / (fmaxf(sqrtf(n1), 1e-8f) * fmaxf(sqrtf(n2), 1e-8f));
-  }
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int col = (lane + 64 * c) * 4;
-    if (col < r) {
-      if (p_out != nullptr) *reinterpret_cast<floatx4 *>(p_out + base + col) = p[c];
-      if (pc_write != nullptr) *reinterpret_cast<floatx4 *>(pc_write + base + col) = p[c];
-    }
   }
 }
 

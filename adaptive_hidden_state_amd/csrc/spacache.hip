@@ -31,7 +31,7 @@ int check_shape(const spa_shape *s, Dims *o) {
   if (s->n_q_heads % s->n_kv_heads != 0) return SPA_ERR_UNSUPPORTED;
   const long long dkv = (long long)s->n_kv_heads * s->head_dim;
   const long long dq = (long long)s->n_q_heads * s->head_dim;
-  if (s->rank % 16 != 0 || s->rank > 1024 || s->rank > s->d_model || s->rank > dkv) return SPA_ERR_UNSUPPORTED;
+  if (s->rank % 16 != 0 || s->rank > s->d_model || s->rank > dkv) return SPA_ERR_UNSUPPORTED;
   // every index computed in 32 bits stays below 2^31
   const long long rows = (long long)s->batch * s->n_tokens;
   long long widest = 2LL * s->d_ffn;

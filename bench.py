@@ -418,13 +418,16 @@ def run_stack(args, wl):
         s = s.replace(rank=s.d_kv)
     elif args.rank:
         s = s.replace(rank=args.rank)
-    L, u, B, N = wl.n_layers, wl.unmask_per_step, s.batch, s.n_tokens
+    L, B, N = wl.n_layers, s.batch, s.n_tokens
+    u = args.unmask or wl.unmask_per_step  # tokens unmasked per denoising step (parallel decoding: more)
+    if u < 1 or u > N:
+        raise SystemExit(f"--unmask must be in 1..{N}")
     rho_p, l_p, rho_1, rho_L = wl.budget
     rhos, ks = spa.spa_budget(L, l_p, rho_p, rho_1, rho_L, N)
     if args.budget == "uniform":
         mean = float(np.mean(rhos))
         ks = spa.spa_budget(1, 1, mean, mean, mean, N)[1] * L
-    steps = args.steps or wl.steps
+    steps = args.steps or N // u
     warmup = 4 if args.warmup is None else args.warmup
     tdt = spa.torch_dtype(s.dtype)
 
@@ -441,7 +444,7 @@ def run_stack(args, wl):
         layers.append(spa.upload_weights(w, w_r, s.dtype))
         del w, w_r
     torch.cuda.synchronize()
-    pos, rows = synth.unmask_schedule(wl, s)
+    pos, rows = synth.unmask_schedule(wl, s, per_step=u)
     rows_neg = -rows
     x0 = synth.normal_device((B, N, s.d_model), wl.config_id, 0, synth.STREAM_X0, dtype=s.dtype)
     x_buf = x0.clone()
@@ -743,6 +746,8 @@ def main():
     ap.add_argument("--identifier", choices=["proxy", "full"], default="proxy",
                     help="stacks: singular proxy, or the full Value projection (r = d_kv)")
     ap.add_argument("--ranks", type=int, nargs="*", default=None, help="batched sweep: proxy ranks")
+    ap.add_argument("--unmask", type=int, default=None,
+                    help="stacks: tokens unmasked per denoising step (default 16 LLaDA, 64 Dream)")
     ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--summarize-counters", metavar="CSV", nargs="*", default=[],
                     help="summarise rocprofv3 counter_collection.csv files and exit")

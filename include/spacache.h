@@ -28,7 +28,8 @@
  *     buffers are safe.
  *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0, d <= 8192 (bf16) or 4096 (fp32);
  *     d_ffn % 16 == 0; head_dim in {64, 128};
- *     n_q_heads % n_kv_heads == 0; 16 <= r <= 1024, r % 16 == 0, r <= min(d, d_kv).
+ *     n_q_heads % n_kv_heads == 0; r % 16 == 0, 16 <= r <= min(d, d_kv) (r = d_kv with W_r = W_v diag(g)
+ *     is the full-dimension Value identifier).
  */
 #ifndef SPACACHE_H
 #define SPACACHE_H

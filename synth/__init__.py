@@ -305,13 +305,14 @@ def normal_device(shape: tuple, config_id: int, layer: int, stream: int, device=
     return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
-def unmask_schedule(wl: Workload, shape: Optional[LayerShape] = None, device="cuda"):
-    """Denoising schedule of a stack workload: T = N / u steps, step t unmasks the u positions
+def unmask_schedule(wl: Workload, shape: Optional[LayerShape] = None, device="cuda", per_step: Optional[int] = None):
+    """Denoising schedule of a stack workload: T = N / u steps (u = per_step, default the workload's),
+    step t unmasks the u positions
     perm[t u : (t + 1) u] of one seeded permutation of the N positions, and gives them fresh N(0, 1)
     embedding rows. Returns (positions T x u int64, rows T x B x u x d in the storage dtype)."""
     import torch
     s = shape or wl.shape
-    u = wl.unmask_per_step
+    u = per_step or wl.unmask_per_step
     t_steps = s.n_tokens // u
     g = _torch_gen(wl.config_id, 0, STREAM_DRIFT, device)
     perm = torch.randperm(s.n_tokens, generator=g, device=device)[: t_steps * u].reshape(t_steps, u)

@@ -230,6 +230,33 @@ def test_identify_scores_and_proxy(shape):
     assert np.array_equal(host(pc), case.cache0.p)        # identify never writes the cache
 
 
+def test_identify_full_value_identifier():
+    """The full-dimension Value identifier: W_r = W_v diag(g_attn), r = d_kv = 2048 (past the 1024
+    columns a wave covers in one pass), two sequences of a ragged length."""
+    import torch
+    spa = _lib()
+    s = synth.LayerShape(2, 200, 2048, 16, 16, 128, 1024, 2048, "bf16")
+    case = Case(s, seed=61, n_drift=50, warm="kv")
+    w_r = synth.to_storage(np.asarray(case.w["w_v"], np.float64) * np.asarray(case.w["g_attn"], np.float64)[None, :],
+                           s.dtype)
+    pc = oracle.proxy(case.x0, w_r).astype(np.float32).astype(np.float64)
+    p_out = torch.empty(s.batch, s.n_tokens, s.rank, dtype=torch.float32, device="cuda")
+    scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
+    pc_d = torch.from_numpy(pc.astype(np.float32)).cuda()
+    spa.spa_identify(s, dev(case.x1, s.dtype), spa.spa_pack_weight(dev(w_r, s.dtype)), pc_d, p_out, scores,
+                     spa.alloc_workspace(s, 0))
+    torch.cuda.synchronize()
+    p_o, s_o = oracle.identify(case.x1, w_r, pc)
+    assert np.max(np.abs(host(scores) - s_o)) <= 1e-3
+    assert rel_l2(host(p_out), p_o) <= 1e-5
+
+
+@pytest.mark.timeout(600)
+def test_layer_step_full_rank_identifier():
+    """A cached step whose identifier has the full Value rank (r = d_kv = 2048)."""
+    s = synth.LayerShape(1, 256, 2048, 16, 16, 128, 1024, 2048, "bf16")
+    _check_step(Case(s, seed=62, n_drift=40, warm="kv"), 64)
+
 @pytest.mark.parametrize("dtype,hd,hq,hkv,n,m", [("bf16", 128, 4, 4, 1024, 256), ("bf16", 64, 6, 2, 77, 13),
                                                  ("f32", 64, 4, 4, 64, 16), ("f32", 128, 2, 1, 100, 70),
                                                  ("bf16", 128, 28, 4, 300, 65)])
