@@ -16,7 +16,13 @@ arXiv 2602.02544):
 
 Readings where the pages are silent (each listed in the design notes of the repository):
   * The block is a pre-norm LLaMA-style layer: RMSNorm -> QKV -> bidirectional SDPA -> W_o ->
-    residual -> RMSNorm -> SwiGLU FFN -> residual. No RoPE, no biases.
+    residual -> RMSNorm -> SwiGLU FFN -> residual. By default no RoPE and no biases (the pages name
+    neither). Optionally, for fidelity to the real architectures (the weights dict carries
+    "rope_theta" and/or "b_q", "b_k", "b_v"): biases are added to q, k, v, then q and k of every
+    head get the rotary position embedding at the token's index in its sequence, in the
+    adjacent-pair form (dims 2j and 2j + 1 rotate by pos * theta^(-2j / head_dim)); K^c caches
+    the rotated keys. A checkpoint written in the half-split pairing converts to this one by a fixed
+    permutation of each head's rows of W_q and W_k (and b_q, b_k), which leaves every q . k unchanged.
   * The proxy reads the raw layer input h ([PN] Phase 1 feeds the input hidden state to the
     projection); the attention RMSNorm gain is folded into W_r, and the row scale of RMSNorm drops
     out of the cosine.
@@ -41,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "round_bf16", "store", "budget", "singular_proxy", "proxy", "cosine", "order_key",
-    "select_topk", "rmsnorm", "silu", "attention", "full_layer", "kv_project", "warmup", "sparse_update",
+    "select_topk", "rmsnorm", "silu", "rope", "attention", "full_layer", "kv_project", "warmup", "sparse_update",
     "cached_layer_step", "LayerCache", "POLICY_ALL", "POLICY_SELECTED",
 ]
 
@@ -217,6 +223,43 @@ def _heads(w: Dict[str, np.ndarray], hd: int):
     return hq, hkv
 
 
+def rope(x: np.ndarray, positions, theta: float) -> np.ndarray:
+    """Rotary position embedding of x (n, heads, head_dim) at integer positions (n,): the pair of
+    dims (2j, 2j + 1) of every head rotates by the angle pos * theta^(-2j / head_dim)."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    inv = float(theta) ** (-2.0 * np.arange(hd // 2, dtype=np.float64) / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None, None] * inv[None, None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def _qkv(a: np.ndarray, w: Dict[str, np.ndarray], positions, head_dim: int):
+    """q, k, v of normalised rows a (n, d) at the given sequence positions: projections, the
+    optional biases, then the optional RoPE on q and k. Returns (n, heads, head_dim) arrays."""
+    n = a.shape[0]
+    hq, hkv = _heads(w, head_dim)
+    q = a @ np.asarray(w["w_q"], np.float64).T
+    k = a @ np.asarray(w["w_k"], np.float64).T
+    v = a @ np.asarray(w["w_v"], np.float64).T
+    if "b_q" in w:
+        q = q + np.asarray(w["b_q"], np.float64)
+        k = k + np.asarray(w["b_k"], np.float64)
+        v = v + np.asarray(w["b_v"], np.float64)
+    q = q.reshape(n, hq, head_dim)
+    k = k.reshape(n, hkv, head_dim)
+    v = v.reshape(n, hkv, head_dim)
+    theta = float(w.get("rope_theta", 0.0))
+    if theta > 0.0:
+        q = rope(q, positions, theta)
+        k = rope(k, positions, theta)
+    return q, k, v
+
+
 def full_layer(x: np.ndarray, w: Dict[str, np.ndarray], head_dim: int, eps: float,
                dtype: str = "f64"):
     """Full forward of the block over every token of every sequence (vanilla decoding).
@@ -232,12 +275,10 @@ def full_layer(x: np.ndarray, w: Dict[str, np.ndarray], head_dim: int, eps: floa
     hc = np.empty((b, n, d))
     for bi in range(b):
         a = rmsnorm(x[bi], w["g_attn"], eps)
-        q = a @ np.asarray(w["w_q"], np.float64).T
-        k = a @ np.asarray(w["w_k"], np.float64).T
-        v = a @ np.asarray(w["w_v"], np.float64).T
-        kc[bi] = store(k.reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
-        vc[bi] = store(v.reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
-        o = attention(q.reshape(n, hq, head_dim), kc[bi], vc[bi])
+        q, k, v = _qkv(a, w, np.arange(n), head_dim)
+        kc[bi] = store(k.transpose(1, 0, 2), dtype)
+        vc[bi] = store(v.transpose(1, 0, 2), dtype)
+        o = attention(q, kc[bi], vc[bi])
         y = x[bi] + o @ np.asarray(w["w_o"], np.float64).T
         bb = rmsnorm(y, w["g_ffn"], eps)
         z = silu(bb @ np.asarray(w["w_gate"], np.float64).T) * (bb @ np.asarray(w["w_up"], np.float64).T)
@@ -257,8 +298,9 @@ def kv_project(x: np.ndarray, w: Dict[str, np.ndarray], head_dim: int, eps: floa
     vc = np.empty((b, hkv, n, head_dim))
     for bi in range(b):
         a = rmsnorm(x[bi], w["g_attn"], eps)
-        kc[bi] = store((a @ np.asarray(w["w_k"], np.float64).T).reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
-        vc[bi] = store((a @ np.asarray(w["w_v"], np.float64).T).reshape(n, hkv, head_dim).transpose(1, 0, 2), dtype)
+        _, k, v = _qkv(a, w, np.arange(n), head_dim)
+        kc[bi] = store(k.transpose(1, 0, 2), dtype)
+        vc[bi] = store(v.transpose(1, 0, 2), dtype)
     return kc, vc
 
 
@@ -288,12 +330,10 @@ def sparse_update(x: np.ndarray, w: Dict[str, np.ndarray], cache: LayerCache, id
             continue
         xi = x[bi, I]
         a = rmsnorm(xi, w["g_attn"], eps)
-        q = a @ np.asarray(w["w_q"], np.float64).T
-        k = a @ np.asarray(w["w_k"], np.float64).T
-        v = a @ np.asarray(w["w_v"], np.float64).T
-        out.k[bi][:, I, :] = store(k.reshape(len(I), hkv, head_dim).transpose(1, 0, 2), dtype)
-        out.v[bi][:, I, :] = store(v.reshape(len(I), hkv, head_dim).transpose(1, 0, 2), dtype)
-        o = attention(q.reshape(len(I), hq, head_dim), out.k[bi], out.v[bi])
+        q, k, v = _qkv(a, w, I, head_dim)
+        out.k[bi][:, I, :] = store(k.transpose(1, 0, 2), dtype)
+        out.v[bi][:, I, :] = store(v.transpose(1, 0, 2), dtype)
+        o = attention(q, out.k[bi], out.v[bi])
         y = xi + o @ np.asarray(w["w_o"], np.float64).T
         bb = rmsnorm(y, w["g_ffn"], eps)
         z = silu(bb @ np.asarray(w["w_gate"], np.float64).T) * (bb @ np.asarray(w["w_up"], np.float64).T)
