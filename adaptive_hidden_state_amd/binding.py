@@ -35,12 +35,12 @@ class spa_shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_tokens", ctypes.c_int32), ("d_model", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("d_ffn", ctypes.c_int32), ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
 
 
 class spa_layer_weights(ctypes.Structure):
     _fields_ = [("w_r", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p), ("w_o", ctypes.c_void_p),
-                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p)]
 
 
 class spa_layer_cache(ctypes.Structure):
@@ -114,9 +114,11 @@ def torch_dtype(dtype):
 
 
 def make_shape(s) -> spa_shape:
-    """spa_shape from any object with the LayerShape attributes (batch, n_tokens, ..., dtype, norm_eps)."""
+    """spa_shape from any object with the LayerShape attributes (batch, n_tokens, ..., dtype, norm_eps,
+    optionally rope_theta)."""
     return spa_shape(int(s.batch), int(s.n_tokens), int(s.d_model), int(s.n_q_heads), int(s.n_kv_heads),
-                     int(s.head_dim), int(s.d_ffn), int(s.rank), dtype_code(s.dtype), float(s.norm_eps))
+                     int(s.head_dim), int(s.d_ffn), int(s.rank), dtype_code(s.dtype), float(s.norm_eps),
+                     float(getattr(s, "rope_theta", 0.0)))
 
 
 def _ptr(t, dtype=None, name="tensor"):
@@ -146,6 +148,7 @@ class DeviceWeights(NamedTuple):
     w_o: object        # d x d_q
     w_gate_up: object  # 2F x d, times diag(g_ffn)
     w_down: object     # d x F
+    b_qkv: object = None  # optional d_q + 2 d_kv biases [b_q; b_k; b_v] (plain vector, storage dtype)
 
 
 class DeviceCache(NamedTuple):
@@ -170,6 +173,11 @@ def _weights_struct(w: DeviceWeights, tdt, shape=None) -> spa_layer_weights:
                 "w_down": (s.d_model, s.d_ffn, SPA_PACK_PLAIN)}
         for f, (r, c, kind) in need.items():
             _check_bytes(getattr(w, f), spa_packed_weight_bytes(s.dtype, r, c, kind), f)
+    if w.b_qkv is not None and shape is not None:
+        s = shape
+        need = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim
+        if w.b_qkv.dim() != 1 or w.b_qkv.numel() != need:
+            raise ValueError(f"b_qkv must be a vector of {need} biases")
     return spa_layer_weights(*(_ptr(getattr(w, f), tdt, f) for f in DeviceWeights._fields))
 
 
@@ -376,8 +384,11 @@ def upload_weights(w: dict, w_r, dtype, device="cuda") -> DeviceWeights:
                           col_scale=g_attn)
     gu = spa_pack_weight(torch.cat([dev(w["w_gate"]), dev(w["w_up"])], 0).contiguous(), SPA_PACK_GATE_UP,
                          col_scale=g_ffn)
+    b_qkv = None
+    if "b_q" in w:   # q, k, v biases, added after the normalisation (not scaled by the gain)
+        b_qkv = torch.cat([dev(w["b_q"]).reshape(-1), dev(w["b_k"]).reshape(-1), dev(w["b_v"]).reshape(-1)]).contiguous()
     out = DeviceWeights(spa_pack_weight(dev(w_r)), qkv, spa_pack_weight(dev(w["w_o"])), gu,
-                        spa_pack_weight(dev(w["w_down"])))
+                        spa_pack_weight(dev(w["w_down"])), b_qkv)
     torch.cuda.current_stream().synchronize()   # the row-major staging copies are freed after packing
     return out
 

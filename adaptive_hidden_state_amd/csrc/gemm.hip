@@ -71,24 +71,54 @@ __device__ __forceinline__ void write_ss32(const EpiArgs &ea, int m, int n0, int
   if (valid && first) ea.ss_out[(size_t)m * (N / 32) + n0 / 32] = ss;
 }
 
+// Rotary embedding of head dims e .. e + 7 (e even) at position pos: the pair (2j, 2j + 1) rotates by
+// pos * theta^(-2j / hd). The angle is taken in revolutions and reduced to [0, 1) before the hardware
+// sine and cosine (which take revolutions); the fp32 product pos * frequency bounds the accuracy
+// (about 1e-3 rad at position 16383), below one bf16 step of the rotated values.
+__device__ __forceinline__ void rope8(float *v, int pos, int e, int hd, float log2_theta) {
+  constexpr float kInvTwoPi = 0.15915494309189535f;
+#pragma unroll
+  for (int x = 0; x < 8; x += 2) {
+    float rev = (float)pos * (exp2f(-(float)(e + x) / (float)hd * log2_theta) * kInvTwoPi);
+    rev -= floorf(rev);
+    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+    const float a = v[x], c = v[x + 1];
+    v[x] = a * cs - c * sn;
+    v[x + 1] = a * sn + c * cs;
+  }
+}
+
 template <typename T, int KIND>
 __device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const float *v, float *ssq = nullptr) {
   if constexpr (KIND == kEpiQKV) {
-    if (n0 < ea.dq) {
-      store8((T *)ea.out + (size_t)m * ea.dq + n0, v);
-      return;
+    float w8[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) w8[x] = v[x];
+    if (ea.bias != nullptr) {
+      float bb[8];
+      load8((const T *)ea.bias + n0, bb);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) w8[x] += bb[x];
     }
     int b;
-    const int i = map_token(ea, m, b);
+    const int i = map_token(ea, m, b);  // the row's token index: its position
+    const bool rope = ea.rope_log2_theta > 0.f;
+    if (n0 < ea.dq) {
+      if (rope) rope8(w8, i, n0 % ea.hd, ea.hd, ea.rope_log2_theta);
+      store8((T *)ea.out + (size_t)m * ea.dq + n0, w8);
+      return;
+    }
     if ((unsigned)i >= (unsigned)ea.n_tok) return;
     int nn = n0 - ea.dq;
     T *dst = (T *)ea.out2;
-    if (nn >= ea.dkv) {
+    const bool is_k = nn < ea.dkv;
+    if (!is_k) {
       nn -= ea.dkv;
       dst = (T *)ea.out3;
     }
     const int g = nn / ea.hd, e = nn - g * ea.hd;
-    store8(dst + (((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e, v);
+    if (is_k && rope) rope8(w8, i, e, ea.hd, ea.rope_log2_theta);
+    store8(dst + (((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e, w8);
   } else if constexpr (KIND == kEpiResid) {
     int b;
     int i = map_token(ea, m, b);

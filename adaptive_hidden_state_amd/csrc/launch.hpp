@@ -32,6 +32,11 @@ struct EpiArgs {
   int ld_src;
   int ldo;
   int f;
+  // kEpiQKV only: `bias` (d_q + 2 d_kv values of T, nullptr for none) is added after the RMSNorm row
+  // scale; then, when rope_log2_theta > 0, q and k get the rotary embedding at the row's token index
+  // (dims 2j, 2j + 1 of a head rotate by pos * theta^(-2j / hd); rope_log2_theta = log2 theta).
+  const void *bias;
+  float rope_log2_theta;
   // RMSNorm fused into the A operand (kinds kEpiQKV and kEpiSwiGLU): A rows are the raw hidden rows
   // (gathered through idx when it is set), the RMSNorm gain is folded into the packed weight, and
   // each output row is scaled by 1 / sqrt(mean(a^2) + norm_eps) over the norm_d columns of A. The

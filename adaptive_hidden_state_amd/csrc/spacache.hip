@@ -15,6 +15,7 @@ namespace {
 struct Dims {
   int B, N, d, hq, hkv, hd, F, Fp, r, dq, dkv, e, dtype;
   float eps;
+  float rope_log2;  // log2(rope_theta), or 0 without rotary embedding
 };
 
 int check_shape(const spa_shape *s, Dims *o) {
@@ -23,6 +24,8 @@ int check_shape(const spa_shape *s, Dims *o) {
       s->head_dim < 1 || s->d_ffn < 1 || s->rank < 1)
     return SPA_ERR_INVALID_ARG;
   if (!(s->norm_eps >= 0.0f) || !isfinite(s->norm_eps)) return SPA_ERR_INVALID_ARG;
+  if (!(s->rope_theta >= 0.0f) || !isfinite(s->rope_theta)) return SPA_ERR_INVALID_ARG;
+  if (s->rope_theta > 0.0f && !(s->rope_theta > 1.0f)) return SPA_ERR_INVALID_ARG;
   if (s->dtype != SPA_F32 && s->dtype != SPA_BF16) return SPA_ERR_UNSUPPORTED;
   if (s->n_tokens > 16384) return SPA_ERR_UNSUPPORTED;
   if (s->d_model % 64 != 0 || s->d_ffn % 16 != 0) return SPA_ERR_UNSUPPORTED;
@@ -52,6 +55,7 @@ int check_shape(const spa_shape *s, Dims *o) {
   o->dtype = s->dtype;
   o->e = s->dtype == SPA_BF16 ? 2 : 4;
   o->eps = s->norm_eps;
+  o->rope_log2 = s->rope_theta > 0.0f ? log2f(s->rope_theta) : 0.0f;
   return SPA_OK;
 }
 
@@ -140,6 +144,7 @@ int check_weights(const spa_layer_weights *w) {
     if (x == nullptr) return SPA_ERR_INVALID_ARG;
     if (!aligned16(x)) return SPA_ERR_ALIGN;
   }
+  if (w->b_qkv != nullptr && !aligned16(w->b_qkv)) return SPA_ERR_ALIGN;  // optional
   return SPA_OK;
 }
 
@@ -213,6 +218,8 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.hd = D.hd;
   qkv.norm_d = D.d;
   qkv.norm_eps = D.eps;
+  qkv.bias = w->b_qkv;
+  qkv.rope_log2_theta = D.rope_log2;
   qkv.row_rinv = (const float *)at(ws, L.rinv);
   const int nqkv = D.dq + 2 * D.dkv;
   const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);

@@ -262,7 +262,7 @@ def run_layer(args, wl):
     import adaptive_hidden_state_amd as spa
     import synth
 
-    s = wl.shape
+    s = wl.shape.replace(rope_theta=wl.arch_rope_theta) if args.arch else wl.shape
     k = int(spa.spa_budget(1, 1, wl.rho, wl.rho, wl.rho, s.n_tokens)[1][0])
     steps = args.steps or 200
     warmup = 10 if args.warmup is None else args.warmup
@@ -270,6 +270,8 @@ def run_layer(args, wl):
     log(f"[bench] generating {wl.name} weights and inputs")
     t = time.time()
     w = synth.layer_weights(wl)
+    if args.arch:
+        w["rope_theta"] = s.rope_theta
     w_r = synth.to_storage(spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], s.rank, w["g_attn"]), s.dtype)
     xs, _ = synth.drift_sequence(wl)
     log(f"[bench] inputs ready in {time.time() - t:.1f} s")
@@ -278,7 +280,7 @@ def run_layer(args, wl):
     # that no step finds the previous step's data in the 256 MB Infinity Cache (one cycle streams > 1 GB)
     R = max(1, args.instances)
     dw0 = spa.upload_weights(w, w_r, s.dtype)
-    dws = [dw0] + [spa.DeviceWeights(*(t.clone() for t in dw0)) for _ in range(R - 1)]
+    dws = [dw0] + [spa.DeviceWeights(*(t.clone() if t is not None else None for t in dw0)) for _ in range(R - 1)]
     tdt = spa.torch_dtype(s.dtype)
     xd0 = [torch.from_numpy(x).to("cuda", tdt).contiguous() for x in xs]
     xds = [xd0] + [[t.clone() for t in xd0] for _ in range(R - 1)]
@@ -352,7 +354,7 @@ def run_layer(args, wl):
                      "hidden states)")
     line["config"] = {"workload": wl.name, "batch": s.batch, "n_tokens": s.n_tokens, "d_model": s.d_model,
                       "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
-                      "d_ffn": s.d_ffn, "rank": s.rank, "rho": wl.rho, "k": k}
+                      "d_ffn": s.d_ffn, "rank": s.rank, "rho": wl.rho, "k": k, "rope_theta": s.rope_theta}
     line["tokens_per_s_projected"] = round(16 * s.batch / (32 * ms_step * 1e-3), 2)
     line["full_recompute_ms"] = round(ms_full, 5)
     line["speedup_vs_full"] = round(ms_full / ms_step, 3)
@@ -400,7 +402,7 @@ def host_weights(w):
     """float32 host copies of a device weight dict (inputs of the CPU oracle baseline)."""
     import numpy as np
     return {key: (v.float().cpu().numpy() if hasattr(v, "device") else np.asarray(v))
-            for key, v in w.items() if key.startswith(("w_", "g_"))}
+            for key, v in w.items() if key.startswith(("w_", "g_", "b_"))}
 
 
 def run_stack(args, wl):
@@ -418,6 +420,9 @@ def run_stack(args, wl):
         s = s.replace(rank=s.d_kv)
     elif args.rank:
         s = s.replace(rank=args.rank)
+    bias = args.arch and wl.arch_qkv_bias
+    if args.arch:
+        s = s.replace(rope_theta=wl.arch_rope_theta)
     L, B, N = wl.n_layers, s.batch, s.n_tokens
     u = args.unmask or wl.unmask_per_step  # tokens unmasked per denoising step (parallel decoding: more)
     if u < 1 or u > N:
@@ -436,7 +441,7 @@ def run_stack(args, wl):
     pair = synth.haar_pair(wl, s)
     layers = []
     for l in range(L):
-        w = synth.layer_weights_device(wl, l + 1, pair, shape=s)
+        w = synth.layer_weights_device(wl, l + 1, pair, shape=s, qkv_bias=bias)
         if args.identifier == "full":   # the full-dimension Value identifier: W_r = W_v diag(g_attn) = W_v
             w_r = w["w_v"]
         else:
@@ -526,6 +531,7 @@ def run_stack(args, wl):
     line["config"] = {"workload": wl.name, "n_layers": L, "batch": B, "n_tokens": N, "d_model": s.d_model,
                       "n_q_heads": s.n_q_heads, "n_kv_heads": s.n_kv_heads, "head_dim": s.head_dim,
                       "d_ffn": s.d_ffn, "rank": s.rank, "identifier": args.identifier, "budget": args.budget,
+                      "rope_theta": s.rope_theta, "qkv_bias": bias,
                       "rho_peak_lpeak_first_last": list(wl.budget), "k_per_layer": ks,
                       "mean_k": round(float(np.mean(ks)), 2), "unmask_per_step": u}
     line["layer_steps_per_s"] = round(L * B / (ms_step * 1e-3), 2)
@@ -543,11 +549,11 @@ def run_stack(args, wl):
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline_sample(wl, s, pair, ks, [0, l_p - 1, L - 1], x0, pos, rows,
-                                                   args.cpu_seconds, args.identifier)
+                                                   args.cpu_seconds, args.identifier, bias)
     return line
 
 
-def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, identifier):
+def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, identifier, bias=False):
     """The oracle's cached step on a sample of one stack's layers (each with its own k_l), from the
     step-0 embeddings and the first unmasking step, within a bounded time."""
     import numpy as np
@@ -561,13 +567,14 @@ def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, 
     x1h = x1.float().cpu().numpy().astype(np.float64)
     done, el = 0, 0.0
     for l in sample_layers:
-        w = synth.layer_weights_device(wl, l + 1, pair, shape=s)
+        w = synth.layer_weights_device(wl, l + 1, pair, shape=s, qkv_bias=bias)
         if identifier == "full":
             w_r = w["w_v"].float().cpu().numpy().astype(np.float64)
         else:
             w_r = spa.singular_proxy_from_factors(w["v_lambda"], w["v_right"], s.rank, w["g_attn"])
             w_r = synth.to_storage(w_r.cpu().numpy(), s.dtype).astype(np.float64)
         wh = host_weights(w)
+        wh["rope_theta"] = s.rope_theta
         del w
         kc, vc = oracle.kv_project(x0h, wh, s.head_dim, s.norm_eps, s.dtype)
         pc = oracle.proxy(x0h, w_r).astype(np.float32).astype(np.float64)
@@ -746,6 +753,9 @@ def main():
     ap.add_argument("--identifier", choices=["proxy", "full"], default="proxy",
                     help="stacks: singular proxy, or the full Value projection (r = d_kv)")
     ap.add_argument("--ranks", type=int, nargs="*", default=None, help="batched sweep: proxy ranks")
+    ap.add_argument("--arch", action="store_true",
+                    help="the real layers' attention terms: rotary embedding (LLaDA theta 5e5, Dream 1e6) and "
+                         "Dream's q/k/v biases")
     ap.add_argument("--unmask", type=int, default=None,
                     help="stacks: tokens unmasked per denoising step (default 16 LLaDA, 64 Dream)")
     ap.add_argument("--summarize-trace", metavar="CSV", help="summarise a rocprofv3 kernel_trace.csv and exit")

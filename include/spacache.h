@@ -70,6 +70,10 @@ typedef struct {
   int32_t rank;        /* r: rows of the singular proxy W_r                          */
   int32_t dtype;       /* spa_dtype                                                  */
   float norm_eps;      /* RMSNorm epsilon                                            */
+  float rope_theta;    /* > 1: rotary embedding of q and k at each token's index in its sequence,
+                          dims (2j, 2j + 1) of a head rotated by pos * rope_theta^(-2j / hd), applied
+                          before K is cached (LLaDA / Dream attention); 0: none. Not from the pages:
+                          an option for fidelity to the real layers.                   */
 } spa_shape;
 
 /* Fragment-packed weight layout. The GEMM weights below are passed packed, once per model, by
@@ -108,6 +112,9 @@ typedef struct {
   const void *w_o;        /* packed d x d_q                                                       */
   const void *w_gate_up;  /* packed SPA_PACK_GATE_UP of [W_gate; W_up] (2F x d), col_scale g_ffn  */
   const void *w_down;     /* packed d x F                                                         */
+  const void *b_qkv;      /* NULL, or d_q + 2 d_kv biases [b_q; b_k; b_v] (plain, storage dtype),
+                             added to q, k, v after the normalisation, before the rotary embedding
+                             (Dream's attention has them)                                          */
 } spa_layer_weights;
 
 /* Per-layer caches (device, read-write), owned by the caller across steps. */

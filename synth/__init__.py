@@ -43,6 +43,7 @@ class LayerShape:
     rank: int
     dtype: str = "bf16"          # "bf16" or "f32": storage type of X, weights, K/V/H caches
     norm_eps: float = 1e-6
+    rope_theta: float = 0.0      # > 1: rotary embedding of q and k (0: none)
 
     @property
     def d_q(self) -> int:
@@ -69,19 +70,21 @@ class Workload:
     drift_range: Optional[tuple] = None     # U(lo, hi) fraction per step
     steps: int = 1                          # cached steps after the warm-up
     unmask_per_step: Optional[int] = None
+    arch_rope_theta: float = 0.0            # the real layers' rotary base (used with the arch option)
+    arch_qkv_bias: bool = False             # the real layers have q/k/v biases
 
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny-f32": Workload(1, "tiny-f32", LayerShape(1, 64, 256, 4, 4, 64, 688, 16, "f32"),
                          rho=0.25, spectrum="geometric0.9", drift_frac=0.2, steps=1),
     "llada-layer": Workload(2, "llada-layer", LayerShape(1, 1024, 4096, 32, 32, 128, 12288, 128, "bf16"),
-                            rho=0.25, spectrum="power1.2", drift_range=(0.1, 0.4), steps=8),
+                            rho=0.25, spectrum="power1.2", drift_range=(0.1, 0.4), steps=8, arch_rope_theta=5e5),
     "llada-stack": Workload(3, "llada-stack", LayerShape(1, 1024, 4096, 32, 32, 128, 12288, 128, "bf16"),
                             n_layers=32, budget=(0.25, 12, 0.05, 0.08), spectrum="power1.2",
-                            steps=64, unmask_per_step=16),
+                            steps=64, unmask_per_step=16, arch_rope_theta=5e5),
     "dream-stack": Workload(4, "dream-stack", LayerShape(1, 2048, 3584, 28, 4, 128, 18944, 128, "bf16"),
                             n_layers=28, budget=(0.25, 10, 0.05, 0.08), spectrum="power1.2",
-                            steps=32, unmask_per_step=64),
+                            steps=32, unmask_per_step=64, arch_rope_theta=1e6, arch_qkv_bias=True),
     "batched-stress": Workload(5, "batched-stress", LayerShape(8, 4096, 4096, 32, 32, 128, 12288, 128, "bf16"),
                                rho=0.25, spectrum="power1.2", drift_frac=0.15, steps=16),
 }
@@ -261,7 +264,7 @@ def haar_pair(wl: Workload, shape: Optional[LayerShape] = None):
 
 
 def layer_weights_device(wl: Workload, layer: int, pair, device="cuda", shape: Optional[LayerShape] = None,
-                         std: float = 0.02) -> Dict[str, object]:
+                         std: float = 0.02, qkv_bias: bool = False) -> Dict[str, object]:
     """Random-init weights of one layer as device tensors in the storage dtype ([out][in] row-major),
     drawn on the device. w_v = (S P U) diag(lambda) (S' P' V)^T with this layer's random row
     permutations P, P' and sign flips S, S' of the shared Haar pair; "v_lambda" (host float64) and
@@ -291,6 +294,8 @@ def layer_weights_device(wl: Workload, layer: int, pair, device="cuda", shape: O
     w["w_v"] = ((u * lam_t[None, :]) @ v.T).to(tdt)
     w["v_lambda"] = np.asarray(lam, dtype=np.float64)
     w["v_right"] = v.T.contiguous()
+    if qkv_bias:   # N(0, std^2) q/k/v biases
+        w["b_q"], w["b_k"], w["b_v"] = normal(1, dq)[0], normal(1, dkv)[0], normal(1, dkv)[0]
     w["g_attn"] = torch.ones(d, dtype=tdt, device=device)
     w["g_ffn"] = torch.ones(d, dtype=tdt, device=device)
     return w

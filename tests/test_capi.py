@@ -97,6 +97,8 @@ def test_workspace_sizes(lib):
     (dict(d_model=4000), -2), (dict(head_dim=96, n_q_heads=32, n_kv_heads=32), -2), (dict(n_kv_heads=5), -2),
     (dict(rank=100), -2), (dict(rank=8192), -2), (dict(rank=4096), 0), (dict(rank=2048, n_kv_heads=8), -2), (dict(n_tokens=20000), -2), (dict(d_ffn=1000), -2),
     (dict(batch=0), -1), (dict(n_tokens=0), -1), (dict(norm_eps=-1.0), -1),
+    (dict(rope_theta=-1.0), -1), (dict(rope_theta=0.5), -1), (dict(rope_theta=float("inf")), -1),
+    (dict(rope_theta=1e6), 0),
     (dict(dtype="f32"), 0), (dict(n_q_heads=28, n_kv_heads=4, d_model=3584), 0)])
 def test_shape_validation(lib, kw, code):
     s = _shape(**kw)

@@ -230,6 +230,70 @@ def test_identify_scores_and_proxy(shape):
     assert np.array_equal(host(pc), case.cache0.p)        # identify never writes the cache
 
 
+def _rope_bias_case(shape, seed, n_drift, bias=True):
+    """A Case whose layer has q/k/v biases (N(0, 0.1^2)) and the rotary embedding of the shape."""
+    case = Case(shape, seed=seed, n_drift=n_drift, warm="kv")
+    rng = np.random.default_rng([96, seed])
+    if bias:
+        for key, n in (("b_q", shape.d_q), ("b_k", shape.d_kv), ("b_v", shape.d_kv)):
+            case.w[key] = synth.to_storage(rng.standard_normal(n) * 0.1, shape.dtype)
+    case.w["rope_theta"] = shape.rope_theta
+    kc, vc = oracle.kv_project(case.x0, case.w, shape.head_dim, EPS, shape.dtype)
+    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), case.cache0.p)
+    return case
+
+
+@pytest.mark.parametrize("shape,k", [
+    (synth.LayerShape(1, 333, 512, 8, 2, 128, 1024, 64, "bf16", rope_theta=1e6), 100),
+    (synth.LayerShape(2, 200, 256, 4, 4, 64, 688, 32, "bf16", rope_theta=1e4), 37),
+    (synth.LayerShape(1, 64, 256, 4, 4, 64, 688, 16, "f32", rope_theta=1e4), 16),
+])
+def test_layer_step_rope_and_biases(shape, k):
+    """Cached steps of layers with q/k/v biases and the rotary embedding (GQA, ragged N, fp32)."""
+    _check_step(_rope_bias_case(shape, 70, shape.n_tokens // 5), k)
+
+
+@pytest.mark.timeout(600)
+def test_layer_step_rope_large_positions():
+    """Positions up to 8191 (the fp32 angle pos * theta^(-2j/hd) at its largest), no biases."""
+    s = synth.LayerShape(1, 8192, 256, 4, 4, 64, 688, 32, "bf16", rope_theta=1e4)
+    _check_step(_rope_bias_case(s, 71, 400, bias=False), 64)
+
+
+def test_layer_full_rope_and_biases():
+    import torch
+    spa = _lib()
+    s = synth.LayerShape(2, 150, 512, 8, 2, 64, 1024, 32, "bf16", rope_theta=5e5)
+    case = _rope_bias_case(s, 72, 30)
+    w, _ = case.device()
+    c = spa.alloc_cache(s)
+    spa.spa_layer_full(s, w, c, dev(case.x1, s.dtype), spa.alloc_workspace(s, s.n_tokens))
+    torch.cuda.synchronize()
+    ref = oracle.warmup(case.x1, case.w, case.w_r, s.head_dim, EPS, s.dtype)
+    errs = {"K": rel_l2(host(c.k), ref.k), "V": rel_l2(host(c.v), ref.v), "H": rel_l2(host(c.h), ref.h)}
+    assert max(errs.values()) <= 2e-2, errs
+
+
+@pytest.mark.timeout(600)
+def test_dream_layer_step_rope_and_biases_full_size():
+    """A full Dream layer (GQA 28/4, N=2048, k=512) with its q/k/v biases and rope_theta = 1e6."""
+    wl = synth.WORKLOADS["dream-stack"]
+    s = wl.shape.replace(rope_theta=1e6)
+    case = Case.__new__(Case)
+    case.shape = s
+    case.w = synth.layer_weights(wl, layer=9)
+    case.w_r = synth.to_storage(oracle.singular_proxy(case.w["w_v"], case.w["g_attn"], s.rank), s.dtype)
+    rng = np.random.default_rng([95, 9])
+    for key, n in (("b_q", s.d_q), ("b_k", s.d_kv), ("b_v", s.d_kv)):
+        case.w[key] = synth.to_storage(rng.standard_normal(n) * 0.1, s.dtype)
+    case.w["rope_theta"] = s.rope_theta
+    case.x0 = synth.first_hidden(wl, layer=9)
+    case.x1, case.drifted = synth.drift_step(case.x0, 600, np.random.default_rng([4, 9, 4]), s.dtype)
+    kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
+    pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
+    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
+    _check_step(case, 512)
+
 def test_identify_full_value_identifier():
     """The full-dimension Value identifier: W_r = W_v diag(g_attn), r = d_kv = 2048 (past the 1024
     columns a wave covers in one pass), two sequences of a ragged length."""
