@@ -19,6 +19,8 @@
 // contiguous range of (sequence, KV head, query head, query block): the blocks that read the same K/V
 // head share that XCD's L2, and HBM sees each head's K/V about once.
 // Query head h reads KV head h / (H_q / H_kv) (grouped-query attention).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -191,7 +193,9 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     }
   };
 
-  auto compute = [&](int t, int buf) {
+  // MASKED: the tile reaches past the last key (only the last tile of a range can)
+  auto compute = [&](int t, int buf, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     const char *ks = stage(buf), *vts = ks + KT * KROWB;
     // S^T block of 32 keys: lane holds query lane%32 and keys 8*(r/4) + 4*(lane/32) + r%4, r = 0..15;
     // two independent MFMA chains over the even and odd head-dim steps
@@ -206,7 +210,7 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     }
     s += s2;
     // raw scores; the softmax scale (and log2 e) is applied inside one FMA per score
-    if (t * KT + KT > n_tok) {  // a tile reaching past the end (uniform branch): mask those keys
+    if constexpr (MASKED) {  // keys past the end score -inf
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = t * KT + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -217,24 +221,30 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
+    // The exponentials are taken against a reference maximum mref that moves only when a query's
+    // maximum exceeds it by more than 8 (so every p <= 2^8, safe in fp32 and in the bf16 P): the
+    // running sums are rescaled rarely instead of on most tiles, and the result is the same softmax.
     const float mnew = fmaxf(mrun, tmax);
-    const float msub = mnew == -INFINITY ? 0.f : mnew;  // no key seen yet: every p is 0
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(fmaf(s[r], scale_log2, -msub));
-      s[r] = p;
-      psum += p;
-    }
-    // rescale the running sums only when some query of this wave raised its maximum
-    if (__any(mnew > mrun)) {
-      const float alpha = exp2f(mrun - mnew);
+    const bool grow = mnew > mrun + 8.f;  // false while no key was seen (-inf)
+    if (__any(grow)) {
+      const float mto = grow ? mnew : mrun;
+      // 1 for queries that keep their reference, 0 from -inf (sums still empty)
+      const float alpha = mto == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mto);
       lrun *= alpha;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) oacc[hb] *= alpha;
+      mrun = mto;
+    }
+    const float msub = mrun == -INFINITY ? 0.f : mrun;  // no key seen yet: every p is 0
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      // hardware 2^x: results below 2^-126 (of a row whose largest p is >= 1) flush to 0
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -msub));
+      s[r] = p;
+      psum += p;
     }
     lrun += psum;
-    mrun = mnew;
 
     // O^T += V^T P^T. In k-step `half` lane group G = lane/32 supplies its scores r = half*8..
     // half*8+7, i.e. keys half*16 + {4G..4G+3, 8+4G..8+4G+3}; A = V^T rows at those keys.
@@ -279,7 +289,11 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
   gload(t_begin + 1);
   if constexpr (QG > 1) __syncthreads();
   for (int i = 0; i < tper; ++i) {
-    compute(t_begin + i, i & 1);
+    const int t = t_begin + i;
+    if (t * KT + KT > n_tok)
+      compute(t, i & 1, std::true_type());
+    else
+      compute(t, i & 1, std::false_type());
     if (i + 1 < tper) {
       lstore((i + 1) & 1);
       gload(t_begin + i + 2);
