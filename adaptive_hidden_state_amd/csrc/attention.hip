@@ -145,24 +145,47 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
   // qg * VW + lane + 64 p, block v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so
   // the lanes that write one V^T row segment hold consecutive key blocks (conflict-free LDS).
   u32x4 rk[KCH], rv[VPER][VB];
-  auto gload = [&](int t) {  // rows past the end are clamped to the last key (masked later)
+  // This lane's element offsets inside a tile (constant over the tiles): K chunk j covers key row
+  // c / (HD / VEC), chunk c % (HD / VEC); V block p covers keys kb VB .. kb VB + VB - 1 of dim chunk cc.
+  // (row = offset / HD, column = offset % HD: HD is a power of two)
+  int koff[KCH], voff[VPER];
+#pragma unroll
+  for (int j = 0; j < KCH; ++j) {
+    const int c = lane + 64 * (j * kAttnQG + qg);
+    koff[j] = (c / (HD / VEC)) * HD + (c % (HD / VEC)) * VEC;
+  }
+#pragma unroll
+  for (int p = 0; p < VPER; ++p) {
+    const int v = min(qg * VW + min(lane + 64 * p, VW - 1), VTASKS - 1);
+    const int kb = v % (KT / VB), cc = v / (KT / VB);
+    voff[p] = kb * VB * HD + cc * VB;
+  }
+  auto gload = [&](int t) {
     const int key0 = t * KT;
+    // tile base (uniform across the wave) + the lane's offset: no per-load address arithmetic
+    const T *kt = kbase + (size_t)key0 * HD;
+    const T *vt = vbase + (size_t)key0 * HD;
+    if (key0 + KT <= n_tok) {  // uniform: the whole tile lies inside the keys
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) {
-      const int c = lane + 64 * (j * kAttnQG + qg);
-      const int row = c / (HD / VEC), col = c % (HD / VEC);
-      const int key = min(key0 + row, n_tok - 1);
-      rk[j] = ld16(reinterpret_cast<const char *>(kbase + (size_t)key * HD) + col * 16);
-    }
+      for (int j = 0; j < KCH; ++j) rk[j] = ld16(kt + koff[j]);
 #pragma unroll
-    for (int p = 0; p < VPER; ++p) {
-      const int v = min(qg * VW + min(lane + 64 * p, VW - 1), VTASKS - 1);
-      const int kb = v % (KT / VB), cc = v / (KT / VB);
+      for (int p = 0; p < VPER; ++p)
 #pragma unroll
-      for (int j = 0; j < VB; ++j) {
-        const int key = min(key0 + kb * VB + j, n_tok - 1);
-        rv[p][j] = ld16(vbase + (size_t)key * HD + cc * VB);
+        for (int j = 0; j < VB; ++j) rv[p][j] = ld16(vt + voff[p] + j * HD);
+    } else {  // a tile reaching past the last key (or wholly past it, in a short key range): rows past
+              // the end read the last key and are masked later
+#pragma unroll
+      for (int j = 0; j < KCH; ++j) {
+        const int key = min(key0 + koff[j] / HD, n_tok - 1);
+        rk[j] = ld16(kbase + (size_t)key * HD + koff[j] % HD);
       }
+#pragma unroll
+      for (int p = 0; p < VPER; ++p)
+#pragma unroll
+        for (int j = 0; j < VB; ++j) {
+          const int key = min(key0 + voff[p] / HD + j, n_tok - 1);
+          rv[p][j] = ld16(vbase + (size_t)key * HD + voff[p] % HD);
+        }
     }
   };
   auto lstore = [&](int buf) {
