@@ -101,13 +101,13 @@ __device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const flo
       for (int x = 0; x < 8; ++x) w8[x] += bb[x];
     }
     int b;
-    const int i = map_token(ea, m, b);  // the row's token index: its position
     const bool rope = ea.rope_log2_theta > 0.f;
     if (n0 < ea.dq) {
-      if (rope) rope8(w8, i, n0 % ea.hd, ea.hd, ea.rope_log2_theta);
+      if (rope) rope8(w8, map_token(ea, m, b), n0 % ea.hd, ea.hd, ea.rope_log2_theta);  // at the token's index
       store8((T *)ea.out + (size_t)m * ea.dq + n0, w8);
       return;
     }
+    const int i = map_token(ea, m, b);  // the row's token index: its position
     if ((unsigned)i >= (unsigned)ea.n_tok) return;
     int nn = n0 - ea.dq;
     T *dst = (T *)ea.out2;
