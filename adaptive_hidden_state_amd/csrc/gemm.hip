@@ -731,6 +731,250 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict_
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Small-M GEMM fed by LDS DMA (bf16; the k-row products of the cached step, M in the hundreds), for
+// the tiles where it beats the register-path kernel (measured on MI355X at M = 256: gate/up 128 x 192
+// ~10% faster, W_down 128 x 128 split 4 ~6%; equal or slower on the narrower tiles). Both operands are
+// copied from global memory into LDS with global_load_lds through a ring of NS 64-k stages. The
+// workgroup has eight waves: waves 4..7 only issue the copies (each its quarter of every stage) and
+// wait for them; waves 0..3 only compute, each a (BM/2) x (BN/2) quarter of the tile from fragments
+// read out of LDS. A copy issue that stalls on a full memory pipeline thus never holds up the MFMA
+// waves, and since the MFMA waves have no copies of their own in flight, the wait for outstanding
+// copies that the compiler places before their LDS reads is immediate, so it schedules those reads
+// freely under the MFMAs. One barrier per stage: the copiers arrive once their share of slab kt has
+// landed, the MFMA waves once they finished slab kt - 1, whose stage then takes slab kt + NS - 1.
+// LDS layout of a stage: A row-major, 128 bytes per row, 16-byte chunks XOR-swizzled by bits 1..3 of
+// the row (conflict-free copies and fragment reads), then the packed weight blocks of the tile's
+// column blocks as stored (four 16-k blocks per column block). A split-K launch writes fp32 partials
+// that splitk_reduce_kernel sums and finishes.
+// ---------------------------------------------------------------------------------------------
+template <int BM, int BN> struct DmaCfg {
+  static constexpr int TM = BM / 2, TN = BN / 2;        // MFMA-wave tile
+  static constexpr int FM = TM / 32, FN = TN / 32;      // its 32x32 blocks
+  static constexpr int A_B = BM * 128, B_B = BN * 128;  // bytes of A and of W in one 64-k stage
+  static constexpr int STAGE = A_B + B_B;
+  static constexpr int NS = 147456 / STAGE < 8 ? 147456 / STAGE : 8;
+  static constexpr int CA = BM / 32, CB = BN / 32;      // copy instructions per copy wave per stage
+  static constexpr int ER = TM < 64 ? TM : 64;          // epilogue rows per pass
+  static constexpr int ES = TN + 4;                     // staged output row (floats)
+  static constexpr int EPI = 4 * ER * ES * 4;
+  static constexpr int BYTES = NS * STAGE > EPI ? NS * STAGE : EPI;
+  static_assert(TM % 32 == 0 && TN % 32 == 0 && BM <= 256 && BN <= 256, "tile shape");
+  static_assert(NS >= 3 && (NS - 1) * (CA + CB) < 64, "ring depth");
+};
+
+// C[m][n] = sum_k A[m][k] W[n][k] over the workgroup's K range (bf16; K and k_split multiples of 64);
+// part != nullptr: fp32 partials of split `split` at part + split M N, else the epilogue KIND.
+template <int BM, int BN, int KIND>
+__global__ __launch_bounds__(512) void gemm_dma_kernel(const bf16_t *__restrict__ A, int lda,
+                                                       const char *__restrict__ W, int wkb, int M, int N, int K,
+                                                       int tiles_m, int tiles_n, int k_split,
+                                                       float *__restrict__ part, EpiArgs ea) {
+  typedef bf16_t T;
+  typedef DmaCfg<BM, BN> C;
+  constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, NS = C::NS, STAGE = C::STAGE;
+  constexpr int CA = C::CA, CB = C::CB, ES = C::ES, ER = C::ER;
+  constexpr bool NORM = KIND == kEpiQKV || KIND == kEpiSwiGLU;
+  static_assert(KIND != kEpiPartial, "the proxy projection stays on the register-path kernel");
+  __shared__ __attribute__((aligned(1024))) char lds[C::BYTES];
+  __shared__ float row_scale[NORM ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool copier = wave >= 4;
+  const int qw = wave & 3;  // quarter of the tile (MFMA waves) or of each stage's copies (copy waves)
+  const int wm = qw & 1, wn = qw >> 1;
+
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int tm = bid % tiles_m;
+  const int rest = bid / tiles_m;
+  const int tn = rest % tiles_n;
+  const int split = rest / tiles_n;
+  const int k0 = split * k_split;
+  const int k1 = min(K, k0 + k_split);
+  const int nk = k1 > k0 ? (k1 - k0) / 64 : 0;
+
+  // Copy plan. A instruction j of a copy wave covers tile rows r0 .. r0 + 7, r0 = 8 (CA qw + j): lane l
+  // lands at byte 16 l of it (row r0 + l / 8, physical chunk l % 8) and so fetches logical chunk
+  // (l % 8) ^ ((row >> 1) & 7) of the row's 128-byte stage slice. Weight instruction j copies stage
+  // block q = CB qw + j: column block q / 4 of the tile, 16-k step q % 4 (the four steps of a column
+  // block are adjacent in memory).
+  const char *a_src[CA];
+#pragma unroll
+  for (int j = 0; j < CA; ++j) {
+    const int row = (qw * CA + j) * 8 + (lane >> 3);
+    const int m = min(tm * BM + row, M - 1);
+    size_t gr = (size_t)m;
+    if (NORM && ea.idx != nullptr) {  // A rows gathered through the update set
+      int b;
+      const int i = map_token(ea, m, b);
+      gr = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+    }
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    a_src[j] = reinterpret_cast<const char *>(A + gr * lda + k0) + chunk * 16;
+  }
+  const int cb_last = (N + 31) / 32 - 1;
+  const char *b_src[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int q = qw * CB + j;
+    const int cb = min(tn * (BN / 32) + (q >> 2), cb_last);
+    b_src[j] = W + ((size_t)cb * wkb + k0 / 16 + (q & 3)) * 1024 + lane * 16;
+  }
+  auto issue = [&](int kt, char *dst) {
+    const int kc = min(kt, nk - 1);
+#pragma unroll
+    for (int j = 0; j < CA; ++j) copy_to_lds(a_src[j] + (size_t)kc * 128, dst + (qw * CA + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) copy_to_lds(b_src[j] + (size_t)kc * 4096, dst + C::A_B + (qw * CB + j) * 1024);
+  };
+
+  if (NORM && !copier) {  // RMSNorm row scales from the producers' statistics (as gemm_kernel)
+    if (ea.row_rinv != nullptr) {
+      for (int r = tid; r < BM; r += 256) {
+        const int m = min(tm * BM + r, M - 1);
+        size_t src = (size_t)m;
+        if (ea.idx != nullptr) {
+          int b;
+          const int i = map_token(ea, m, b);
+          src = (size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1);
+        }
+        row_scale[r] = ea.row_rinv[src];
+      }
+    } else {
+      constexpr int TPR = 256 / BM;
+      const int r = tid / TPR, part_i = tid % TPR;
+      const int m = min(tm * BM + r, M - 1);
+      const floatx4 *ps = reinterpret_cast<const floatx4 *>(ea.ss_in + (size_t)m * ea.ss_n);
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = part_i; j < ea.ss_n / 4; j += TPR) v += ps[j];
+      float t = (v[0] + v[1]) + (v[2] + v[3]);
+      if constexpr (TPR >= 2) t += __shfl_xor(t, 1, kWave);
+      if constexpr (TPR >= 4) t += __shfl_xor(t, 2, kWave);
+      if (part_i == 0) row_scale[r] = 1.0f / sqrtf(t / (float)ea.norm_d + ea.norm_eps);
+    }
+  }
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  if (nk > 0) {
+    // fragment offsets inside a stage: A row wm TM + 32 i + lane % 32, logical chunk 2 s + lane / 32
+    // (swizzled); weight block (column block wn FN + j, k-step s)
+    const int sw = ((lane & 31) >> 1) & 7;
+    const int arow = (wm * TM + (lane & 31)) * 128;
+    int a_off[4], b_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a_off[s] = arow + ((2 * s + (lane >> 5)) ^ sw) * 16;
+      b_off[s] = C::A_B + (wn * FN * 4 + s) * 1024 + lane * 16;
+    }
+    if (copier) {
+#pragma unroll
+      for (int u = 0; u < NS - 1; ++u) issue(u, lds + u * STAGE);
+    }
+    int cur = 0;  // stage of slab kt
+    for (int kt = 0; kt < nk; ++kt) {
+      if (copier) wait_vmem<(NS - 2) * (CA + CB)>();  // this wave's copies of slab kt landed
+      __builtin_amdgcn_s_barrier();  // everyone's did, and everyone finished reading slab kt - 1
+      if (copier) {
+        issue(kt + NS - 1, lds + (cur == 0 ? NS - 1 : cur - 1) * STAGE);
+      } else {
+        const char *st = lds + cur * STAGE;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u32x4 af[FM], bf[FN];
+#pragma unroll
+          for (int i = 0; i < FM; ++i) af[i] = ld16(st + a_off[s] + i * 4096);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) bf[j] = ld16(st + b_off[s] + j * 4096);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+        }
+      }
+      cur = cur == NS - 1 ? 0 : cur + 1;
+    }
+    if (copier) wait_vmem<0>();  // no copy may land in LDS after this point
+  }
+  __syncthreads();
+  if (copier) return;
+
+  // Epilogue in passes of ER rows per MFMA wave: stage row-major in the wave's own LDS region (the
+  // wave reads back only what it wrote), then every lane finishes eight consecutive columns of a row.
+  float *ep = reinterpret_cast<float *>(lds) + qw * ER * ES;
+#pragma unroll
+  for (int h = 0; h < TM / ER; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < ER / 32; ++ii)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          ep[(ii * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3)) * ES + j * 32 + (lane & 31)] =
+              acc[h * (ER / 32) + ii][j][q];
+    const int rbase = wm * TM + h * ER;  // row of the tile
+    const int mbase = tm * BM + rbase, nbase = tn * BN + wn * TN;
+    if (part != nullptr) {
+      EpiArgs pe{};
+      pe.out = part + (size_t)split * M * N;
+      pe.ldo = N;
+      for (int idx = lane; idx < ER * TN / 8; idx += 64) {
+        const int lr = idx / (TN / 8), c8 = idx - lr * (TN / 8);
+        const int m = mbase + lr, n0 = nbase + c8 * 8;
+        if (m < M && n0 < N) epi8<T, kEpiPartial>(pe, m, n0, ep + lr * ES + c8 * 8);
+      }
+    } else if constexpr (KIND == kEpiSwiGLU) {
+      // columns 32 c + 0..15 are the gate rows of units 16 c + 0..15, columns 32 c + 16..31 their up rows
+      for (int idx = lane; idx < ER * TN / 16; idx += 64) {
+        const int lr = idx / (TN / 16), g8 = idx - lr * (TN / 16);
+        const int c = g8 >> 1, hh = g8 & 1;
+        const int m = mbase + lr, j0 = (nbase / 32 + c) * 16 + hh * 8;
+        const float *row = ep + lr * ES + c * 32 + hh * 8;
+        if (m < M && j0 < ea.f) {
+          float g[8], u[8];
+          const float sc = row_scale[rbase + lr];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            g[x] = row[x] * sc;
+            u[x] = row[16 + x] * sc;
+          }
+          epi8_swiglu<T>(ea, m, j0, g, u);
+        }
+      }
+    } else {
+      for (int idx = lane; idx < ER * TN / 8; idx += 64) {  // uniform trip count (ER TN / 8 % 64 == 0)
+        const int lr = idx / (TN / 8), c8 = idx - lr * (TN / 8);
+        const int m = mbase + lr, n0 = nbase + c8 * 8;
+        if constexpr (KIND == kEpiResid) {  // chunks c8 & ~3 .. c8 | 3 share a 32-column block
+          float ss = 0.f;
+          const bool valid = m < M && n0 < N;
+          if (valid) epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8, &ss);
+          if (ea.ss_out != nullptr) write_ss32(ea, m, n0, N, ss, valid, (c8 & 3) == 0);
+        } else if (m < M && n0 < N) {
+          if constexpr (NORM) {
+            float v[8];
+            const float sc = row_scale[rbase + lr];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) v[x] = ep[lr * ES + c8 * 8 + x] * sc;
+            epi8<T, KIND>(ea, m, n0, v);
+          } else {
+            epi8<T, KIND>(ea, m, n0, ep + lr * ES + c8 * 8);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order (deterministic), then the epilogue, eight columns (or
 // eight hidden units) per thread.
 template <typename T, int KIND>
@@ -848,6 +1092,16 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       best.k_split = K;
     }
   }
+  // The 128-row tiles run on the LDS-DMA kernel (same tile and split): measured over M = 64 .. 1024 on
+  // the llada and Dream shapes it takes 0.82 .. 0.98 of the register-path time there, while on the
+  // 64-row tiles it is level or slower.
+  if (dtype == kBF16 && kind != kEpiPartial && K % 64 == 0 && best.k_split % 64 == 0) {
+    for (int i = 0; i < kDmaTileCount; ++i)
+      if (best.cfg < kBigTileCfg && kDmaTiles[i][0] == best.bm && kDmaTiles[i][1] == best.bn) {
+        best.cfg = kDmaCfg0 + i;
+        break;
+      }
+  }
   best.tiles_m = ceil_div(M, best.bm);
   best.tiles_n = ceil_div(N, best.bn);
   return best;
@@ -873,6 +1127,25 @@ static hipError_t run_gemm(const GemmPlan &p, const void *A, int lda, const void
   return hipGetLastError();
 }
 
+template <int BM, int BN, int KIND>
+static hipError_t run_dma(const GemmPlan &p, const void *A, int lda, const void *W, int wkb, int M, int N, int K,
+                          float *part, const EpiArgs &ea, hipStream_t s) {
+  if constexpr (KIND == kEpiPartial) {
+    return hipErrorInvalidValue;
+  } else {
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, KIND>), dim3(grid), dim3(512), 0, s, (const bf16_t *)A, lda,
+                       (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, p.k_split, p.splits > 1 ? part : nullptr,
+                       ea);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || p.splits == 1) return err;
+    const size_t work = (KIND == kEpiSwiGLU ? (size_t)M * ea.f : (size_t)M * N) / 8;
+    const unsigned rgrid = (unsigned)((work + 255) / 256);
+    hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t, KIND>), dim3(rgrid), dim3(256), 0, s, part, p.splits, M, N, ea);
+    return hipGetLastError();
+  }
+}
+
 template <typename T, int KIND>
 static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void *W, int wkb, int M, int N, int K,
                           float *part, const EpiArgs &ea, hipStream_t s) {
@@ -892,6 +1165,9 @@ static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void 
           return hipGetLastError();
         }
         return hipErrorInvalidValue;
+      case kDmaCfg0 + 0: return run_dma<128, 192, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case kDmaCfg0 + 1: return run_dma<128, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
+      case kDmaCfg0 + 2: return run_dma<128, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
       default: return run_gemm<T, 64, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
     }
   }

@@ -64,6 +64,11 @@ struct GemmPlan {
 
 // Tile configuration of the large-M kernel: bf16 only, 256 x 256 tiles, never split, no kEpiPartial.
 constexpr int kBigTileCfg = 6;
+// Tile configurations of the LDS-DMA small-M kernel (bf16, no kEpiPartial): kDmaCfg0 + i for tiles
+// kDmaTiles[i] (BM x BN).
+constexpr int kDmaCfg0 = 7;
+constexpr int kDmaTileCount = 3;
+constexpr int kDmaTiles[kDmaTileCount][2] = {{128, 192}, {128, 128}, {128, 64}};
 
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
