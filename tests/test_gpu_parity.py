@@ -190,7 +190,8 @@ def test_rho_one_step_equals_full_on_gpu():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("b,n", [(1, 1), (3, 64), (2, 1000), (1, 4096), (2, 16384)])
+@pytest.mark.parametrize("b,n", [(1, 1), (3, 64), (2, 1000), (1, 1024), (2, 1025), (1, 2048), (2, 3000), (1, 4096),
+                                 (1, 4097), (2, 16384)])
 def test_topk_bit_exact(b, n):
     import torch
     spa = _lib()
