@@ -389,6 +389,14 @@ def test_llada_layer_step_full_size(llada_case):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [130, 200])
+def test_llada_layer_step_full_size_ragged_rows(llada_case, k):
+    """Update sets whose row count is not a multiple of the 128-row GEMM tiles: gate/up and W_down run
+    on the LDS-DMA kernel with a last row tile of 2 (k = 130) or 72 (k = 200) valid rows."""
+    _check_step(llada_case, k)
+
+
+@pytest.mark.timeout(600)
 def test_dream_layer_step_full_size():
     wl = synth.WORKLOADS["dream-stack"]
     s = wl.shape
