@@ -186,6 +186,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wk = wave >> 1;
+  if (ea.clear != nullptr && blockIdx.x == 0)
+    for (int i = tid; i < ea.clear_n; i += 256) ea.clear[i] = 0u;
 
   int bid = blockIdx.x;
   const int nb = gridDim.x;

@@ -16,14 +16,14 @@ namespace spa {
 // columns (16-byte accesses; r % 16 == 0), so any rank works, up to the full Value width. Each lane
 // reads its columns of the cached proxy before it writes the same columns, so the cache may be
 // updated in place (pc_write == pc_read).
-__global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
-                                                           int r, const float *pc_read, float *pc_write,
-                                                           float *__restrict__ p_out, float *__restrict__ scores,
-                                                           const float *__restrict__ ss_part, int d, float eps,
-                                                           float *__restrict__ rinv) {
+// One token per wave: its proxy row (split partials summed in order), the cosine against P^c, the
+// P^c / P writes and its 1 / rms.
+template <bool COHERENT = false>
+__device__ __forceinline__ void cosine_row(const float *__restrict__ part, int splits, int rows, int r, int row,
+                                           const float *pc_read, float *pc_write, float *__restrict__ p_out,
+                                           float *scores, const float *__restrict__ ss_part, int d, float eps,
+                                           float *__restrict__ rinv) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
   const size_t plane = (size_t)rows * r;
   const size_t base = (size_t)row * r;
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
@@ -53,8 +53,24 @@ __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restri
     dot = wave_sum(dot);
     n1 = wave_sum(n1);
     n2 = wave_sum(n2);
-    if (lane == 0) scores[row] = dot / (fmaxf(sqrtf(n1), 1e-8f) * fmaxf(sqrtf(n2), 1e-8f));
+    const float c = dot / (fmaxf(sqrtf(n1), 1e-8f) * fmaxf(sqrtf(n2), 1e-8f));
+    if (lane == 0) {
+      if constexpr (COHERENT)
+        __hip_atomic_store(scores + row, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        scores[row] = c;
+    }
   }
+}
+
+__global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
+                                                           int r, const float *pc_read, float *pc_write,
+                                                           float *__restrict__ p_out, float *__restrict__ scores,
+                                                           const float *__restrict__ ss_part, int d, float eps,
+                                                           float *__restrict__ rinv) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  cosine_row(part, splits, rows, r, row, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv);
 }
 
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read, float *pc_write,
@@ -65,6 +81,7 @@ hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, c
                      pc_write, p_out, scores, ss_part, d, eps, rinv);
   return hipGetLastError();
 }
+
 
 // rinv[row] = 1 / sqrt(mean(x_row^2) + eps) over d columns; one wave per row (for the sparse update
 // called without the identification pass that otherwise produces these scales).
@@ -158,36 +175,49 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 // would otherwise pile every key into one histogram bin); the rest is resolved with digits of up to
 // 11 bits, stopping as soon as the selected bin fits exactly. Equal keys at the boundary are taken in
 // index order.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int n, int k,
-                                                            int32_t *__restrict__ idx_out) {
-  constexpr int kBins = 2048;
-  __shared__ uint32_t hist[2][kBins];
-  __shared__ uint32_t wsum[16], wand[16], wor[16];
-  __shared__ uint32_t sel_prefix, sel_krem, sel_full;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float *s = scores + (size_t)b * n;
-  int32_t *out = idx_out + (size_t)b * k;
-  const int chunk = (n + kTopkThreads - 1) / kTopkThreads;
+struct TopkShared {
+  static constexpr int kBins = 2048;
+  uint32_t hist[2][kBins];
+  uint32_t wsum[16], wand[16], wor[16];
+  uint32_t sel_prefix, sel_krem, sel_full;
+};
+
+// The k smallest of the n scores s[0 .. n) by a workgroup of TH threads (TH PER >= n), indices written
+// ascending to out[0 .. k). Every thread of the workgroup calls it (it has barriers).
+// COHERENT: the scores were written by other workgroups in the same launch with agent-scope atomic
+// stores; they are read with agent-scope atomic loads (no stale cached copy).
+template <int TH, int PER, bool COHERENT = false>
+__device__ void topk_block(const float *s, int n, int k, int32_t *out, TopkShared &sh) {
+  static_assert(TH % 64 == 0 && TH <= 1024 && TopkShared::kBins % TH == 0 && PER <= 64, "top-k block shape");
+  constexpr int kBins = TopkShared::kBins;
+  uint32_t(&hist)[2][kBins] = sh.hist;
+  uint32_t *wsum = sh.wsum, *wand = sh.wand, *wor = sh.wor;
+  uint32_t &sel_prefix = sh.sel_prefix, &sel_krem = sh.sel_krem, &sel_full = sh.sel_full;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = (n + TH - 1) / TH;
   const int start = tid * chunk;
   if (k >= n) {  // every token
-    for (int i = tid; i < n; i += kTopkThreads) out[i] = i;
+    for (int i = tid; i < n; i += TH) out[i] = i;
     return;
   }
 
-  uint32_t key[kTopkPerThread];
-  uint32_t valid = 0, kand = 0xffffffffu, kor = 0u;
+  uint32_t key[PER];
+  uint64_t valid = 0;
+  uint32_t kand = 0xffffffffu, kor = 0u;
 #pragma unroll
-  for (int j = 0; j < kTopkPerThread; ++j) {
+  for (int j = 0; j < PER; ++j) {
     const int i = start + j;
     const bool ok = j < chunk && i < n;
-    key[j] = ok ? order_key(s[i]) : 0u;
-    valid |= (ok ? 1u : 0u) << j;
+    float v = 0.f;
+    if (ok) v = COHERENT ? __hip_atomic_load(s + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : s[i];
+    key[j] = ok ? order_key(v) : 0u;
+    valid |= (ok ? 1ull : 0ull) << j;
     if (ok) {
       kand &= key[j];
       kor |= key[j];
     }
   }
-  for (int i = tid; i < 2 * kBins; i += kTopkThreads) (&hist[0][0])[i] = 0u;
+  for (int i = tid; i < 2 * kBins; i += TH) (&hist[0][0])[i] = 0u;
   kand = wave_and(kand);
   kor = wave_or(kor);
   if (lane == 0) {
@@ -198,7 +228,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
   kand = 0xffffffffu;
   kor = 0u;
 #pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
+  for (int w = 0; w < TH / 64; ++w) {
     kand &= wand[w];
     kor |= wor[w];
   }
@@ -214,24 +244,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
     const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
     uint32_t *h = hist[pass & 1];
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j)
-      if (((valid >> j) & 1u) && (key[j] & above) == prefix) atomicAdd(&h[(key[j] >> lo) & dmask], 1u);
+    for (int j = 0; j < PER; ++j)
+      if (((valid >> j) & 1ull) && (key[j] & above) == prefix) atomicAdd(&h[(key[j] >> lo) & dmask], 1u);
     __syncthreads();
-    // two bins per thread; inclusive counts by a block scan
-    const uint32_t v0 = h[2 * tid], v1 = h[2 * tid + 1];
+    // BPT consecutive bins per thread; inclusive counts by a block scan
+    constexpr int BPT = kBins / TH;
+    uint32_t v[BPT], tot = 0;
     uint32_t *hn = hist[(pass + 1) & 1];  // next pass's bins (last read one pass ago)
-    hn[2 * tid] = 0u;
-    hn[2 * tid + 1] = 0u;
-    const uint32_t e0 = block_exclusive_scan(v0 + v1, wsum);
-    const uint32_t i0 = e0 + v0, i1 = i0 + v1;
-    if (e0 < krem && krem <= i0) {
-      sel_prefix = prefix | ((uint32_t)(2 * tid) << lo);
-      sel_krem = krem - e0;
-      sel_full = (i0 == krem) ? 1u : 0u;
-    } else if (i0 < krem && krem <= i1) {
-      sel_prefix = prefix | ((uint32_t)(2 * tid + 1) << lo);
-      sel_krem = krem - i0;
-      sel_full = (i1 == krem) ? 1u : 0u;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      v[q] = h[BPT * tid + q];
+      hn[BPT * tid + q] = 0u;
+      tot += v[q];
+    }
+    uint32_t e = block_exclusive_scan(tot, wsum);
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const uint32_t i1 = e + v[q];
+      if (e < krem && krem <= i1) {
+        sel_prefix = prefix | ((uint32_t)(BPT * tid + q) << lo);
+        sel_krem = krem - e;
+        sel_full = (i1 == krem) ? 1u : 0u;
+      }
+      e = i1;
     }
     __syncthreads();
     prefix = sel_prefix;
@@ -250,13 +285,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
   if (!full) {
     uint32_t ceq = 0;
 #pragma unroll
-    for (int j = 0; j < kTopkPerThread; ++j) ceq += (((valid >> j) & 1u) && (key[j] & mask) == prefix) ? 1u : 0u;
+    for (int j = 0; j < PER; ++j) ceq += (((valid >> j) & 1ull) && (key[j] & mask) == prefix) ? 1u : 0u;
     r = block_exclusive_scan(ceq, wsum);
   }
-  uint32_t sel = 0, csel = 0;
+  uint64_t sel = 0;
+  uint32_t csel = 0;
 #pragma unroll
-  for (int j = 0; j < kTopkPerThread; ++j) {
-    if (!((valid >> j) & 1u)) continue;
+  for (int j = 0; j < PER; ++j) {
+    if (!((valid >> j) & 1ull)) continue;
     const uint32_t km = key[j] & mask;
     bool take = km < prefix;
     if (km == prefix) {
@@ -264,14 +300,87 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
       ++r;
     }
     if (take) {
-      sel |= 1u << j;
+      sel |= 1ull << j;
       ++csel;
     }
   }
   uint32_t pos = block_exclusive_scan(csel, wsum);
 #pragma unroll
-  for (int j = 0; j < kTopkPerThread; ++j)
-    if (((sel >> j) & 1u) && pos < (uint32_t)k) out[pos++] = start + j;
+  for (int j = 0; j < PER; ++j)
+    if (((sel >> j) & 1ull) && pos < (uint32_t)k) out[pos++] = start + j;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int n, int k,
+                                                            int32_t *__restrict__ idx_out) {
+  __shared__ TopkShared sh;
+  const int b = blockIdx.x;
+  topk_block<kTopkThreads, kTopkPerThread>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
+}
+
+// The cosine pass fused with the Top-k of each sequence (n tokens per sequence, k of them selected):
+// every workgroup scores four tokens as proxy_cosine_kernel, then adds the number of its tokens in each
+// sequence to that sequence's counter; the workgroup whose addition completes a sequence runs the
+// Top-k of that sequence (topk_block, 256 threads) and resets its counter to 0. The scores cross
+// workgroups through agent-scope atomic stores and loads, which are coherent across the XCDs' L2
+// caches without cache-wide write-backs or invalidations (release / acquire fences would flush the
+// whole L2, including this kernel's P^c writes); each wave waits until its score store has completed
+// before the workgroup's counter addition, which is itself an agent-scope atomic, and the Top-k's
+// loads are issued only after that addition returned the completing count. The counters must be 0 at
+// launch (the proxy projection that precedes this kernel clears them).
+template <int PER>
+__global__ __launch_bounds__(256) void cosine_topk_kernel(const float *__restrict__ part, int splits, int rows,
+                                                          int r, const float *pc_read, float *pc_write,
+                                                          float *__restrict__ p_out, float *scores,
+                                                          const float *__restrict__ ss_part, int d, float eps,
+                                                          float *__restrict__ rinv, int n, int k,
+                                                          int32_t *__restrict__ idx_out, uint32_t *counters) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t last[4];
+  const int tid = threadIdx.x, row0 = blockIdx.x * 4;
+  const int row = row0 + (tid >> 6);
+  if (row < rows) cosine_row<true>(part, splits, rows, r, row, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's memory operations (its score store included) completed
+  __syncthreads();
+  if (tid == 0) {  // the (at most four) sequences of this workgroup's rows, in order
+    int nl = 0;
+    for (int rr = row0; rr < min(row0 + 4, rows);) {
+      const int b = rr / n;
+      const int end = min(min(row0 + 4, rows), (b + 1) * n);
+      const uint32_t cnt = (uint32_t)(end - rr);
+      const uint32_t before = __hip_atomic_fetch_add(&counters[b], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (before + cnt == (uint32_t)n) last[nl++] = (uint32_t)b;
+      rr = end;
+    }
+    for (int j = nl; j < 4; ++j) last[j] = 0xffffffffu;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t b = last[j];  // uniform
+    if (b == 0xffffffffu) break;
+    topk_block<256, PER, true>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
+    if (tid == 0) __hip_atomic_store(&counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();  // the shared state is reused by the next sequence
+  }
+}
+
+hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, int r, const float *pc_read,
+                              float *pc_write, float *p_out, float *scores, const float *ss_part, int d, float eps,
+                              float *rinv, int k, int32_t *idx_out, uint32_t *counters, hipStream_t s) {
+  const int rows = batch * n;
+  if (rows <= 0) return hipSuccess;
+  if (n > 64 * 256 || k <= 0 || pc_read == nullptr || scores == nullptr) return hipErrorInvalidValue;
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (n <= 4 * 256)
+    hipLaunchKernelGGL(cosine_topk_kernel<4>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
+  else if (n <= 16 * 256)
+    hipLaunchKernelGGL(cosine_topk_kernel<16>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
+  else
+    hipLaunchKernelGGL(cosine_topk_kernel<64>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s) {

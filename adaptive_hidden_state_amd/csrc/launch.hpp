@@ -52,6 +52,10 @@ struct EpiArgs {
   // elements in the split's K range to ss_out[split * M + m]; kEpiResid with ss_out set writes the sum
   // of squares of each row's stored outputs per 32 columns to ss_out[m * (N / 32) + n / 32].
   float *ss_out;
+  // Register-path kernel only: workgroup 0 sets clear[0 .. clear_n) to 0 (counters that the next
+  // kernel on the stream expects at 0).
+  uint32_t *clear;
+  int clear_n;
 };
 
 struct GemmPlan {
@@ -113,6 +117,12 @@ hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const voi
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,
                                float *pc_write, float *p_out, float *scores, const float *ss_part, int d,
                                float eps, float *rinv, hipStream_t s);
+// The same cosine pass fused with the Top-k of each of the batch sequences (n <= 16384 tokens each,
+// 1 <= k): idx_out (batch x k) as launch_topk; counters (batch entries) must be 0 at launch and are
+// left 0.
+hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, int r, const float *pc_read,
+                              float *pc_write, float *p_out, float *scores, const float *ss_part, int d, float eps,
+                              float *rinv, int k, int32_t *idx_out, uint32_t *counters, hipStream_t s);
 // rinv[row] = 1 / sqrt(mean(x_row^2) + eps) for rows x d.
 hipError_t launch_row_rinv(int dtype, const void *x, int rows, int d, float eps, float *rinv, hipStream_t s);
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s);

@@ -71,7 +71,7 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Workspace regions. Offsets are multiples of 256 bytes.
 struct Layout {
   GemmPlan proxy;
-  size_t ppart, pbuf, scores, ssp, rinv, q, o, y, z, ss32, gpart, total;
+  size_t ppart, pbuf, scores, ssp, rinv, counters, q, o, y, z, ss32, gpart, total;
 };
 
 Layout make_layout(const Dims &D, int k_max) {
@@ -90,6 +90,7 @@ Layout make_layout(const Dims &D, int k_max) {
   L.scores = take(rows * 4);
   L.ssp = take((size_t)L.proxy.splits * rows * 4);  // per-split sums of squares of the hidden rows
   L.rinv = take(rows * 4);                          // their 1 / rms (attention RMSNorm)
+  L.counters = take((size_t)D.B * 4);               // per-sequence counters of the fused Top-k
   L.q = take(m * D.dq * D.e);
   L.o = take(m * D.dq * D.e);
   L.y = take(m * D.d * D.e);
@@ -176,19 +177,43 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
 }
 
 // Phase 1 on device: proxy GEMM (fp32 split-K partials) then reduce + cosine + writes.
+// Phase 1. With k > 0 (and pc_read, scores set) the Top-k of every sequence is taken too (idx_out,
+// B x k): up to kFusedTopkRows hidden rows inside the cosine kernel, beyond that (where the waiting of
+// every wave for its stores before the counter update, repeated over many rounds of waves, costs more
+// than the separate launch saves; measured at 32768 rows) by the Top-k kernel after it. With k = 0
+// only the scores.
+constexpr int kFusedTopkRows = 8192;
+
 int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w_r, const float *pc_read,
-                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s, Marks &mk) {
+                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s, Marks &mk, int k = 0,
+                 int32_t *idx_out = nullptr) {
   const int rows = D.B * D.N;
   float *part = (float *)at(ws, L.ppart);
   float *ssp = (float *)at(ws, L.ssp), *rinv = (float *)at(ws, L.rinv);
+  uint32_t *counters = (uint32_t *)at(ws, L.counters);
+  const bool topk = k > 0 && rows <= kFusedTopkRows;
   EpiArgs ea{};
   ea.ss_out = ssp;  // the projection streams every hidden row: it also sums their squares
+  if (topk) {       // and clears the Top-k counters of the cosine kernel that follows
+    ea.clear = counters;
+    ea.clear_n = D.B;
+  }
   SPA_TRY(launch_gemm(D.dtype, kEpiPartial, L.proxy, h_in, D.d, w_r, packed_wkb(D.dtype, D.d), rows, D.r, D.d, part,
                       ea, s));
   SPA_TRY(mk.mark("proxy_gemm"));
-  SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, ssp, D.d, D.eps,
-                              rinv, s));
-  SPA_TRY(mk.mark("proxy_cosine"));
+  if (topk) {
+    SPA_TRY(launch_cosine_topk(part, L.proxy.splits, D.B, D.N, D.r, pc_read, pc_write, p_out, scores, ssp, D.d, D.eps,
+                               rinv, k, idx_out, counters, s));
+    SPA_TRY(mk.mark("cosine_topk"));
+  } else {
+    SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, ssp, D.d, D.eps,
+                                rinv, s));
+    SPA_TRY(mk.mark("proxy_cosine"));
+    if (k > 0) {
+      SPA_TRY(launch_topk(scores, D.B, D.N, k, idx_out, s));
+      SPA_TRY(mk.mark("topk"));
+    }
+  }
   return SPA_OK;
 }
 
@@ -392,11 +417,9 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
   Marks mk{timing, stream};
   SPA_TRY(mk.mark("start"));
   if ((st = run_identify(D, L, h_in, w->w_r, cache->p_cache, sel ? nullptr : cache->p_cache, sel ? pbuf : nullptr,
-                         scores, ws, stream, mk)) != SPA_OK)
+                         scores, ws, stream, mk, k, idx_out)) != SPA_OK)
     return st;
   if (k == 0) return SPA_OK;
-  SPA_TRY(launch_topk(scores, D.B, D.N, k, idx_out, stream));
-  SPA_TRY(mk.mark("topk"));
   if (sel) {
     SPA_TRY(launch_copy_selected(pbuf, cache->p_cache, idx_out, D.B, D.N, k, D.r, stream));
     SPA_TRY(mk.mark("proxy_copy_selected"));

@@ -142,6 +142,8 @@ def kernel_work(name, s, k):
         return (rows * s.d_model + s.rank * s.d_model) * e + rows * s.rank * 4, 2.0 * rows * s.d_model * s.rank
     if name == "proxy_cosine":
         return rows * s.rank * 4 * 3 + rows * 4, 6.0 * rows * s.rank
+    if name == "cosine_topk":     # the cosine pass plus the Top-k (scores re-read, indices written)
+        return rows * s.rank * 4 * 3 + rows * 4 * 2 + M * 4, 6.0 * rows * s.rank
     if name == "topk":
         return rows * 4 + M * 4, 0.0
     if name == "attention":
@@ -218,7 +220,13 @@ def ideal_floor_us(work, peak_flops):
 
 
 GEMM_KERNELS = ("qkv_gemm_scatter", "wo_gemm_residual", "gate_up_gemm_swiglu", "down_gemm_scatter")
-STEP_KERNELS = ("proxy_gemm", "proxy_cosine", "topk") + GEMM_KERNELS[:1] + ("attention",) + GEMM_KERNELS[1:]
+STEP_KERNELS = ("proxy_gemm", "cosine_topk") + GEMM_KERNELS[:1] + ("attention",) + GEMM_KERNELS[1:]
+SPLIT_IDENTIFY = ("proxy_gemm", "proxy_cosine", "topk") + GEMM_KERNELS[:1] + ("attention",) + GEMM_KERNELS[1:]
+
+
+def step_kernels(s):
+    """Kernel names of one cached step: the Top-k runs inside the cosine kernel up to 8192 hidden rows."""
+    return STEP_KERNELS if s.batch * s.n_tokens <= 8192 else SPLIT_IDENTIFY
 
 
 def base_line(args, wl, s, value, unit, ms_step, steps, warmup, data):
@@ -347,7 +355,7 @@ def run_layer(args, wl):
 
     per_us = timed_kernels(spa, one, max(10, min(steps, 50)))
     peak_flops = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
-    work = {n: kernel_work(n, s, k) for n in STEP_KERNELS}
+    work = {n: kernel_work(n, s, k) for n in step_kernels(s)}
 
     line = base_line(args, wl, s, s.batch / (ms_step * 1e-3), "layer-steps/s", ms_step, steps, warmup,
                      "synthetic (seeded random-init weights with a planted Value spectrum; drifting N(0,1) "
@@ -508,7 +516,7 @@ def run_stack(args, wl):
     per_us = timed_kernels(spa, one, 3)
     peak_flops = PEAK_BF16_TFLOPS
     work = {}
-    for n in STEP_KERNELS:
+    for n in step_kernels(s):
         b = f = 0.0
         for kl in ks:
             bb, ff = kernel_work(n, s, kl)
@@ -655,7 +663,7 @@ def run_batched(args, wl):
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / steps
-            work = {n: kernel_work(n, s, k) for n in STEP_KERNELS}
+            work = {n: kernel_work(n, s, k) for n in step_kernels(s)}
             floor = ideal_floor_us(work, peak_flops) / 1e3
             pt = {"rank": r, "rho": rho, "k": k, "ms_per_step": round(ms, 4),
                   "layer_steps_per_s": round(B / (ms * 1e-3), 2), "ideal_floor_ms": round(floor, 4),

@@ -160,9 +160,11 @@ int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa
  * events; spa_layer_step_timed records marks[0] on the stream before its first kernel and
  * marks[i + 1] right after its i-th kernel, stopping when capacity is reached, and sets `count` to
  * the number recorded. names (optional, capacity - 1 entries) receives a static name per kernel:
- * proxy_gemm, proxy_cosine, topk, [proxy_copy_selected], rmsnorm_gather, qkv_gemm_scatter,
- * attention, wo_gemm_residual, rmsnorm, gate_up_gemm_swiglu, down_gemm_scatter (a GEMM that splits
- * K adds a second kernel, its reduce, under the same name). */
+ * proxy_gemm, cosine_topk (the cosine of every token and, in the workgroup that completes a
+ * sequence, its Top-k; up to 8192 rows B N, beyond that proxy_cosine then topk; proxy_cosine alone
+ * when k = 0), [proxy_copy_selected], qkv_gemm_scatter,
+ * attention, wo_gemm_residual, gate_up_gemm_swiglu, down_gemm_scatter (a GEMM that splits K adds a
+ * second kernel, its reduce, under the same name). */
 typedef struct {
   hipEvent_t *marks;
   int32_t capacity;

@@ -213,6 +213,33 @@ def test_topk_bit_exact(b, n):
             assert got[bi].tolist() == oracle.select_topk(s[bi], k).tolist(), (bi, k)
 
 
+@pytest.mark.parametrize("shape", [SMALL_BF16[0], SMALL_BF16[1],
+                                   synth.LayerShape(5, 3, 128, 2, 2, 64, 256, 16, "bf16"),
+                                   synth.LayerShape(3, 1030, 256, 4, 4, 64, 688, 32, "bf16"),
+                                   synth.LayerShape(1, 4100, 256, 4, 4, 64, 688, 32, "bf16")])
+def test_layer_step_fused_topk_equals_spa_topk(shape):
+    """The Top-k taken inside the cosine kernel of spa_layer_step (by the workgroup that completes each
+    sequence) equals spa_topk on the scores that step returns, and the oracle's selection on them:
+    sequences whose tokens share workgroups (N % 4 != 0, N < 4), and the three key-per-thread sizes."""
+    import torch
+    spa = _lib()
+    s = shape
+    case = Case(s, seed=80 + s.n_tokens, n_drift=max(1, s.n_tokens // 5), warm="kv")
+    w, c = case.device()
+    x1 = dev(case.x1, s.dtype)
+    for k in sorted({1, s.n_tokens // 3, s.n_tokens - 1, s.n_tokens} - {0}):
+        idx = torch.full((s.batch, k), -1, dtype=torch.int32, device="cuda")
+        scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
+        spa.spa_layer_step(s, w, c, x1, k, 0, idx, scores, spa.alloc_workspace(s, k))
+        ref = torch.full((s.batch, k), -2, dtype=torch.int32, device="cuda")
+        spa.spa_topk(scores, k, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref), k
+        sc = host(scores)
+        for b in range(s.batch):
+            assert host(idx)[b].tolist() == oracle.select_topk(sc[b], k).tolist(), (b, k)
+
+
 @pytest.mark.parametrize("shape", [synth.WORKLOADS["tiny-f32"].shape, SMALL_BF16[0], SMALL_BF16[1]])
 def test_identify_scores_and_proxy(shape):
     import torch
