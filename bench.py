@@ -133,6 +133,29 @@ def summarize_profile(trace_csv=None, counter_csvs=()):
     return "\n".join(out)
 
 
+def gpu_info():
+    """The device's name, arch, compute units and shader clocks (sysfs DPM table: the highest level and
+    the level current at the time of the call), for the bench line."""
+    import glob
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": torch.cuda.get_device_name(0) or getattr(p, "name", ""),
+            "arch": getattr(p, "gcnArchName", ""), "compute_units": int(p.multi_processor_count)}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                lv = [ln.split() for ln in f.read().splitlines() if "Mhz" in ln]
+        except OSError:
+            continue
+        mhz = [int(x[1].lower().replace("mhz", "")) for x in lv if len(x) >= 2]
+        cur = [int(x[1].lower().replace("mhz", "")) for x in lv if len(x) >= 3 and x[-1] == "*"]
+        if mhz:
+            info["sclk_max_mhz"] = max(mhz)
+            info["sclk_now_mhz"] = cur[0] if cur else None
+            break
+    return info
+
+
 def kernel_work(name, s, k):
     """Algorithmic bytes and flops of one kernel of the cached step (inputs read once, outputs written
     once), for the per-kernel HBM / MFMA fractions."""
@@ -372,7 +395,7 @@ def run_layer(args, wl):
     line["timing"] = {"graphs": graphs is not None, "instances": R,
                       "note": "per-kernel us from HIP events recorded between kernels on the launch stream"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
-    line["gpu"] = torch.cuda.get_device_name(0)
+    line["gpu"] = gpu_info()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(wl, w, np.asarray(w_r, np.float64), xs, k, args.cpu_seconds)
@@ -552,7 +575,7 @@ def run_stack(args, wl):
                       "note": "ms_per_step = one denoising step through all layers (the unmasking copy "
                               "included); per-kernel us summed over the layers of one step"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
-    line["gpu"] = torch.cuda.get_device_name(0)
+    line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -705,7 +728,7 @@ def run_batched(args, wl):
     line["timing"] = {"graphs": False, "instances": 1,
                       "note": "eager launches (steps of milliseconds); per-kernel us at the headline point"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
-    line["gpu"] = torch.cuda.get_device_name(0)
+    line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one sequence")
