@@ -1038,17 +1038,27 @@ constexpr TileCfg kTiles[6] = {{128, 192}, {64, 192}, {128, 128}, {128, 64}, {64
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
 
-// Cost model of one launch in CU clocks, fitted to MI355X measurements of this kernel at M = 256 and
-// 1024 (within ~10%): a workgroup costs its K range times its load time (weight panel from HBM, A
-// tile mostly from L2) plus its MFMA time, which overlap little at one wave per SIMD; workgroups run
-// one per CU in rounds; split-K adds the fp32 partial round trip (~2.6 TB/s) and a second launch.
-double plan_cost(int bm, int bn, int M, int N, int K, int splits, int kc) {
+// Workgroups of the bf16 register-path kernel resident per CU, by tile configuration and epilogue kind
+// (register-limited: each 256-thread workgroup puts one wave on each SIMD).
+constexpr int kRegTileWgsPerCU[6][5] = {{1, 1, 1, 1, 1}, {2, 1, 2, 1, 2}, {1, 1, 1, 1, 1},
+                                        {2, 2, 2, 2, 2}, {2, 2, 2, 2, 2}, {4, 3, 4, 3, 4}};
+
+// Cost model of one launch in CU clocks, fitted to MI355X measurements of these kernels over M = 51 ..
+// 2048 on the llada and Dream shapes (over 85 shapes its picks sum to within 2% of the fastest
+// measured tile and split per shape): a
+// workgroup costs its K range times its load time (weight panel from HBM, A tile mostly from L2) plus
+// its MFMA time, which overlap little; w workgroups resident on a CU share its read path and together
+// run 1.2 (w = 2), 1.3 (3) or 1.4 (4) times as fast as one; split-K adds the fp32 partial round trip
+// (~2.6 TB/s) and a second launch. dma: cost factor of the LDS-DMA kernel that runs the tile (1 = none).
+double plan_cost(int bm, int bn, int M, int N, int K, int splits, int kc, int wpc, double dma) {
+  static const double kShared[5] = {1.0, 1.0, 1.2, 1.3, 1.4};
   const long long tiles = (long long)ceil_div(M, bm) * ceil_div(N, bn);
   const long long wgs = tiles * splits;
-  const double rounds = (double)ceil_div_ll(wgs, kCUs);
-  const double load = (bn + 0.5 * bm) / 14.0;
+  const int w = (int)std::max(1LL, std::min((long long)wpc, ceil_div_ll(wgs, kCUs)));
+  const double rounds = (double)ceil_div_ll(wgs, (long long)kCUs * w);
+  const double load = (bn + 0.6 * bm) / 14.0;
   const double mfma = (double)bm * bn / 1660.0;
-  double t = rounds * kc * (load + mfma);
+  double t = rounds * kc * (load + mfma) * w / kShared[w] * dma;
   if (splits > 1) t += (double)M * N * splits * 0.00646 + 4200.0;
   return t;
 }
@@ -1069,7 +1079,13 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       if (splits > 1 && (kind == kEpiQKV || kind == kEpiSwiGLU)) break;  // fused RMSNorm needs all of K
       if (splits > 1 && kc < 4 * bk) break;       // keep at least four slabs per split
       if (splits > 1 && (long long)ceil_div(M, tc.bm) * ceil_div(N, tc.bn) * splits > kMaxSplitWGs) break;
-      double cost = plan_cost(tc.bm, tc.bn, M, N, K, splits, kc);
+      const bool bf = dtype == kBF16;
+      const int wpc = bf && kind >= 0 && kind < 5 ? kRegTileWgsPerCU[cfg][kind] : 1;
+      // the 128-row tiles run on the LDS-DMA kernel (remapped below); relative to the register-path
+      // model of the same tile its cost is fitted as 0.9 for 128 x 192 and 128 x 128 (level for 128 x 64)
+      const bool dma = bf && kind != kEpiPartial && K % 64 == 0 && kc % 64 == 0 && tc.bm == 128;
+      const double dma_f = dma && tc.bn != 64 ? 0.9 : 1.0;
+      double cost = plan_cost(tc.bm, tc.bn, M, N, K, splits, kc, wpc, dma_f);
       if (kind == kEpiPartial && splits > 1) cost -= 4200.0;  // partials are the output anyway
       if (best.bm == 0 || cost < best_cost) {
         best_cost = cost;
@@ -1094,9 +1110,8 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       best.k_split = K;
     }
   }
-  // The 128-row tiles run on the LDS-DMA kernel (same tile and split): measured over M = 64 .. 1024 on
-  // the llada and Dream shapes it takes 0.82 .. 0.98 of the register-path time there, while on the
-  // 64-row tiles it is level or slower.
+  // The 128-row tiles run on the LDS-DMA kernel (same tile and split); on the 64-row tiles it measured
+  // level or slower.
   if (dtype == kBF16 && kind != kEpiPartial && K % 64 == 0 && best.k_split % 64 == 0) {
     for (int i = 0; i < kDmaTileCount; ++i)
       if (best.cfg < kBigTileCfg && kDmaTiles[i][0] == best.bm && kDmaTiles[i][1] == best.bn) {
