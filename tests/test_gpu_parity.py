@@ -416,18 +416,18 @@ def test_llada_layer_step_full_size(llada_case):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("k", [130, 200])
+@pytest.mark.parametrize("k", [51, 87, 130, 200])
 def test_llada_layer_step_full_size_ragged_rows(llada_case, k):
-    """Update sets whose row count is not a multiple of the 128-row GEMM tiles: gate/up and W_down run
-    on the LDS-DMA kernel with a last row tile of 2 (k = 130) or 72 (k = 200) valid rows."""
+    """Update sets whose row count is not a multiple of the GEMM tiles: at k = 130 and 200 gate/up and
+    W_down run on the LDS-DMA kernel with a last row tile of 2 or 72 valid rows; k = 51 and 87 (the
+    stack's first layers) take the 64-row register-path tiles and split-K W_o."""
     _check_step(llada_case, k)
 
 
-@pytest.mark.timeout(600)
-def test_dream_layer_step_full_size():
+@pytest.fixture(scope="module")
+def dream_case():
     wl = synth.WORKLOADS["dream-stack"]
     s = wl.shape
-    _, ks = oracle.budget(28, 10, 0.25, 0.05, 0.08, s.n_tokens)
     case = Case.__new__(Case)
     case.shape = s
     case.w = synth.layer_weights(wl, layer=9)
@@ -438,7 +438,21 @@ def test_dream_layer_step_full_size():
     kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
     pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
     case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
-    _check_step(case, int(ks[9]))          # layer 10 = the peak: k = 512
+    return case
+
+
+@pytest.mark.timeout(600)
+def test_dream_layer_step_full_size(dream_case):
+    _, ks = oracle.budget(28, 10, 0.25, 0.05, 0.08, dream_case.shape.n_tokens)
+    _check_step(dream_case, int(ks[9]))          # layer 10 = the peak: k = 512
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("k", [102, 311])
+def test_dream_layer_step_full_size_stack_rows(dream_case, k):
+    """Row counts of other Dream stack layers (first layer k = 102; k = 311 on the way to the peak),
+    where the GEMMs take the 64-row register-path tiles with two to four workgroups per CU."""
+    _check_step(dream_case, k)
 
 
 @pytest.mark.timeout(900)
