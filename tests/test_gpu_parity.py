@@ -370,6 +370,30 @@ def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
         assert rel_l2(got[bi], ref) <= tol_for(dtype), rel_l2(got[bi], ref)
 
 
+@pytest.mark.parametrize("b,hd,hq,hkv,n,m", [(8, 128, 32, 32, 333, 450), (8, 128, 32, 4, 1024, 256),
+                                             (4, 64, 64, 16, 100, 700)])
+def test_attend_many_queries_matches_oracle(b, hd, hq, hkv, n, m):
+    """Enough queries per head for the 256-query bf16 kernel (B H_q ceil(m / 256) >= 256 workgroups,
+    query blocks at least 3/4 full): ragged key tiles (333, 100 keys), ragged last query blocks (450,
+    700 queries), GQA groups of 8 and 4, hd 64."""
+    import torch
+    spa = _lib()
+    qb = (m + 255) // 256
+    assert b * hq * qb >= 256 and 4 * m >= 3 * 256 * qb
+    rng = np.random.default_rng([n, m, hq])
+    q = synth.to_storage(rng.standard_normal((b, m, hq, hd)) * 1.5, "bf16")
+    kc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), "bf16")
+    vc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), "bf16")
+    shape = synth.LayerShape(b, n, 256, hq, hkv, hd, 256, 16, "bf16")
+    o = torch.empty(b, m, hq * hd, dtype=torch.bfloat16, device="cuda")
+    spa.spa_attend(shape, dev(q, "bf16"), m, dev(kc, "bf16"), dev(vc, "bf16"), o)
+    torch.cuda.synchronize()
+    got = host(o)
+    for bi in (0, b - 1):
+        ref = oracle.attention(q[bi].astype(np.float64), kc[bi].astype(np.float64), vc[bi].astype(np.float64))
+        assert rel_l2(got[bi], ref) <= tol_for("bf16"), rel_l2(got[bi], ref)
+
+
 def test_sparse_update_unsorted_and_out_of_range_indices():
     import torch
     spa = _lib()
