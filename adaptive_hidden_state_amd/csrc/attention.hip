@@ -522,67 +522,71 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
     }
   };
 
-  // masked: the tile reaches past the last key (a runtime branch: two inlined variants of this body
-  // would not fit the register file)
-  auto compute = [&](int t, int buf, bool masked) {
-    const char *ks = stage(buf), *vts = ks + KT * KROWB;
-    floatx16 s[2];
+  // S^T = K Q^T of the tile in stage buf, both query blocks (each K fragment feeds two MFMAs)
+  auto qk = [&](int buf, floatx16 (&s)[2]) {
+    const char *krow = stage(buf) + (lane & 31) * KROWB + (lane >> 5) * 16;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int jq = 0; jq < 2; ++jq)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[j][r] = 0.f;
-    const char *krow = ks + (lane & 31) * KROWB + (lane >> 5) * 16;
+      for (int r = 0; r < 16; ++r) s[jq][r] = 0.f;
 #pragma unroll
     for (int st = 0; st < QSTEPS; ++st) {
       const u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + st * 32);
       s[0] = mfma32(kf, qf[0][st], s[0]);
       s[1] = mfma32(kf, qf[1][st], s[1]);
     }
+  };
+  // Online softmax of tile t in place (scores -> probabilities). masked: the tile reaches past the
+  // last key (a runtime branch: two inlined variants would not fit the register file).
+  auto softmax = [&](int t, floatx16 (&s)[2], bool masked) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int jq = 0; jq < 2; ++jq) {
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * KT + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (key >= n_tok) s[j][r] = -INFINITY;
+          if (key >= n_tok) s[jq][r] = -INFINITY;
         }
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[j][r]);
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[jq][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
       // reference maximum that moves only when a query's maximum exceeds it by more than 8 (p <= 2^8)
-      const float mnew = fmaxf(mrun[j], tmax);
-      const bool grow = mnew > mrun[j] + 8.f;
+      const float mnew = fmaxf(mrun[jq], tmax);
+      const bool grow = mnew > mrun[jq] + 8.f;
       if (__any(grow)) {
-        const float mto = grow ? mnew : mrun[j];
-        const float alpha = mto == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[j] - mto);
-        lrun[j] *= alpha;
+        const float mto = grow ? mnew : mrun[jq];
+        const float alpha = mto == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[jq] - mto);
+        lrun[jq] *= alpha;
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) oacc[j][hb] *= alpha;
-        mrun[j] = mto;
+        for (int hb = 0; hb < HB; ++hb) oacc[jq][hb] *= alpha;
+        mrun[jq] = mto;
       }
-      const float msub = mrun[j] == -INFINITY ? 0.f : mrun[j];
+      const float msub = mrun[jq] == -INFINITY ? 0.f : mrun[jq];
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][r], scale_log2, -msub));
-        s[j][r] = p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[jq][r], scale_log2, -msub));
+        s[jq][r] = p;
         psum += p;
       }
-      lrun[j] += psum;
+      lrun[jq] += psum;
     }
-    // O^T += V^T P^T, each V^T fragment shared by the two query blocks
+  };
+  // O^T += V^T P^T from the tile in stage buf, each V^T fragment shared by the two query blocks
+  auto pv = [&](int buf, const floatx16 (&s)[2]) {
+    const char *vts = stage(buf) + KT * KROWB;
     const int G = lane >> 5;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       u32x4 pf[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        pf[j][0] = pack_bf16x2(s[j][half * 8 + 0], s[j][half * 8 + 1]);
-        pf[j][1] = pack_bf16x2(s[j][half * 8 + 2], s[j][half * 8 + 3]);
-        pf[j][2] = pack_bf16x2(s[j][half * 8 + 4], s[j][half * 8 + 5]);
-        pf[j][3] = pack_bf16x2(s[j][half * 8 + 6], s[j][half * 8 + 7]);
+      for (int jq = 0; jq < 2; ++jq) {
+        pf[jq][0] = pack_bf16x2(s[jq][half * 8 + 0], s[jq][half * 8 + 1]);
+        pf[jq][1] = pack_bf16x2(s[jq][half * 8 + 2], s[jq][half * 8 + 3]);
+        pf[jq][2] = pack_bf16x2(s[jq][half * 8 + 4], s[jq][half * 8 + 5]);
+        pf[jq][3] = pack_bf16x2(s[jq][half * 8 + 6], s[jq][half * 8 + 7]);
       }
       const int c0 = (half * 16 + 4 * G) * 2, c1 = c0 + 16;
 #pragma unroll
@@ -603,7 +607,10 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
   gload(1);
   __syncthreads();
   for (int i = 0; i < ntiles; ++i) {
-    compute(i, i & 1, i * KT + KT > n_tok);
+    floatx16 s[2];
+    qk(i & 1, s);
+    softmax(i, s, i * KT + KT > n_tok);
+    pv(i & 1, s);
     if (i + 1 < ntiles) {
       lstore((i + 1) & 1);
       gload(i + 2);
