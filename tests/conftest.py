@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 @pytest.fixture(autouse=True)
 def _gpu_progress_log(request):
-    """Before each GPU test, append its id to gpurun_out/test_progress.log (flushed to disk), so a
-    run that ends abruptly still names the case it was in."""
+    """Before each GPU test, append its id to test_progress.log in the run's output folder (flushed
+    to disk), so a run that ends abruptly still names the case it was in."""
     if request.node.get_closest_marker("gpu") is not None:
         out = os.path.join(ROOT, "gpurun_out")
         try:
