@@ -394,6 +394,60 @@ def test_attend_many_queries_matches_oracle(b, hd, hq, hkv, n, m):
         assert rel_l2(got[bi], ref) <= tol_for("bf16"), rel_l2(got[bi], ref)
 
 
+def test_three_layer_chain_matches_oracle():
+    """Three layers chained as the stack workloads run them (layer l reads layer l-1's H^c; one
+    workspace and one index / score buffer shared by the layers): the warm-up chain (spa_layer_full)
+    and one cached-step chain (spa_layer_step) against the oracle's chain, layer by layer. k is the
+    number of drifted tokens, whose cosines lie far below the rest at every layer (the later layers'
+    other input rows are exactly their cached rows), so both sides select the same sets."""
+    import torch
+    spa = _lib()
+    s = synth.LayerShape(2, 200, 256, 4, 4, 64, 688, 32, "bf16")
+    L, n_drift = 3, 30
+    ws = [synth.random_weights(s, seed=500 + l, std=0.1, gains="random") for l in range(L)]
+    wrs = [synth.to_storage(oracle.singular_proxy(w["w_v"], w["g_attn"], s.rank), s.dtype) for w in ws]
+    x0 = synth.random_hidden(s, seed=599)
+    x1, drifted = synth.drift_step(x0, n_drift, np.random.default_rng([5, 99]), s.dtype)
+
+    caches_o, x = [], x0
+    for l in range(L):
+        caches_o.append(oracle.warmup(x, ws[l], wrs[l], s.head_dim, EPS, s.dtype))
+        x = caches_o[l].h
+    dws = [spa.upload_weights(ws[l], wrs[l], s.dtype) for l in range(L)]
+    dcs = [spa.alloc_cache(s) for _ in range(L)]
+    wsp = spa.alloc_workspace(s, s.n_tokens)
+    xd = dev(x0, s.dtype)
+    for l in range(L):
+        spa.spa_layer_full(s, dws[l], dcs[l], xd, wsp)
+        xd = dcs[l].h
+    torch.cuda.synchronize()
+    warm_h = [host(dcs[l].h) for l in range(L)]
+    for l in range(L):
+        assert rel_l2(warm_h[l], caches_o[l].h) <= 2e-2, l
+
+    idx = torch.empty(s.batch, n_drift, dtype=torch.int32, device="cuda")
+    scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
+    got_idx, xd = [], dev(x1, s.dtype)
+    for l in range(L):
+        spa.spa_layer_step(s, dws[l], dcs[l], xd, n_drift, spa.SPA_PROXY_WRITE_ALL, idx, scores, wsp)
+        got_idx.append(host(idx).astype(np.int64))
+        xd = dcs[l].h
+    torch.cuda.synchronize()
+
+    x = x1
+    for l in range(L):
+        new, idx_o, _ = oracle.cached_layer_step(x, ws[l], wrs[l], caches_o[l], n_drift, s.head_dim, EPS, s.dtype)
+        hh = host(dcs[l].h)
+        for b in range(s.batch):
+            I = np.sort(np.asarray(idx_o[b], np.int64))
+            assert np.array_equal(I, drifted[b]), (l, b)
+            assert np.array_equal(np.sort(got_idx[l][b]), I), (l, b)
+            assert rel_l2(hh[b][I], new.h[b][I]) <= tol_for(s.dtype), (l, b)
+            rest = np.setdiff1d(np.arange(s.n_tokens), I)
+            assert np.array_equal(hh[b][rest], warm_h[l][b][rest]), (l, b)
+        x = new.h
+
+
 def test_sparse_update_unsorted_and_out_of_range_indices():
     import torch
     spa = _lib()
