@@ -149,7 +149,7 @@ __device__ __forceinline__ void epi8_swiglu(const EpiArgs &ea, int m, int j0, co
   float z[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) z[x] = g[x] / (1.0f + __expf(-g[x])) * u[x];
-  store8((T *)ea.out + (size_t)m * ea.f + j0, z);
+  store8((T *)ea.out + (size_t)m * (ea.ldz ? ea.ldz : ea.f) + j0, z);
 }
 
 template <int BM, int BN> struct GemmLds {
@@ -1064,7 +1064,9 @@ double plan_cost(int bm, int bn, int M, int N, int K, int splits, int kc, int wp
 }
 }  // namespace
 
-GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
+namespace {
+// Best register-path or LDS-DMA plan (no 256 x 256 tiles) and its modelled cost.
+GemmPlan plan_small(int dtype, int M, int N, int K, int kind, double *cost_out) {
   GemmPlan best{};
   const int bk = dtype == kF32 ? 32 : 64;
   double best_cost = 0.0;
@@ -1097,30 +1099,66 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
       }
     }
   }
-  // The 256 x 256 kernel (bf16, no split): one 32-k slab per ~70 clocks when its tiles fit in one
-  // round, ~75 under full load (measured over M = 256 .. 8192, N = 3584 .. 37888); it wins once the
-  // tiles fill the chip.
-  if (dtype == kBF16 && kind != kEpiPartial) {
-    const long long tiles = (long long)ceil_div(M, 256) * ceil_div(N, 256);
-    const double cost = (double)ceil_div_ll(tiles, kCUs) * K * (tiles <= kCUs ? 70.0 : 75.0);
-    if (cost < best_cost) {
-      best.cfg = kBigTileCfg;
-      best.bm = best.bn = 256;
-      best.splits = 1;
-      best.k_split = K;
-    }
-  }
   // The 128-row tiles run on the LDS-DMA kernel (same tile and split); on the 64-row tiles it measured
   // level or slower.
   if (dtype == kBF16 && kind != kEpiPartial && K % 64 == 0 && best.k_split % 64 == 0) {
     for (int i = 0; i < kDmaTileCount; ++i)
-      if (best.cfg < kBigTileCfg && kDmaTiles[i][0] == best.bm && kDmaTiles[i][1] == best.bn) {
+      if (kDmaTiles[i][0] == best.bm && kDmaTiles[i][1] == best.bn) {
         best.cfg = kDmaCfg0 + i;
         break;
       }
   }
   best.tiles_m = ceil_div(M, best.bm);
   best.tiles_n = ceil_div(N, best.bn);
+  *cost_out = best_cost;
+  return best;
+}
+
+// The 256 x 256 kernel (bf16, no split): one 32-k slab per ~70 clocks when its tiles fit in one round,
+// ~75 under full load (measured over M = 256 .. 8192, N = 3584 .. 37888).
+double big_cost(int M, int N, int K) {
+  const long long tiles = (long long)ceil_div(M, 256) * ceil_div(N, 256);
+  return (double)ceil_div_ll(tiles, kCUs) * K * (tiles <= kCUs ? 70.0 : 75.0);
+}
+}  // namespace
+
+GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
+  double cost;
+  GemmPlan best = plan_small(dtype, M, N, K, kind, &cost);
+  if (dtype != kBF16 || kind == kEpiPartial) return best;
+  GemmPlan big{};
+  big.cfg = kBigTileCfg;
+  big.bm = big.bn = 256;
+  big.splits = 1;
+  big.k_split = K;
+  big.tiles_m = ceil_div(M, 256);
+  big.tiles_n = ceil_div(N, 256);
+  // the 256 x 256 kernel wins once its tiles fill the chip
+  const double c_big = big_cost(M, N, K);
+  if (c_big < cost) {
+    best = big;
+    cost = c_big;
+  }
+  // SwiGLU at up to 512 rows with a last round of 256 x 256 tiles less than half full: the columns of
+  // the whole rounds on the 256 x 256 kernel, the rest on the best smaller tile (measured on the Dream
+  // gate/up at M = 512: 142 + 31 us against 210 for the best single launch, at M = 428 132 + 31
+  // against 189; at M = 2616 on the llada gate/up it measured level to 1.5% slower, so larger M keep
+  // one launch)
+  const long long tiles = (long long)big.tiles_m * big.tiles_n;
+  if (kind == kEpiSwiGLU && big.tiles_m <= 2 && tiles > kCUs && tiles % kCUs < kCUs / 2) {
+    const int tn0 = (int)((tiles / kCUs) * kCUs / big.tiles_m);  // tile columns of the whole rounds
+    if (tn0 > 0 && tn0 < big.tiles_n) {
+      const int n0 = tn0 * 256;
+      double c_tail;
+      plan_small(dtype, M, N - n0, K, kind, &c_tail);
+      const double c_split = big_cost(M, n0, K) + c_tail;
+      if (c_split < cost) {
+        best = big;
+        best.tiles_n = tn0;
+        best.n_main = n0;
+      }
+    }
+  }
   return best;
 }
 
@@ -1206,6 +1244,24 @@ static hipError_t run_kind(int kind, const GemmPlan &p, const void *A, int lda, 
 hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W, int wkb,
                        int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (plan.n_main > 0) {  // SwiGLU: whole rounds of 256 x 256 tiles, then the remaining columns
+    const int n0 = plan.n_main;
+    if (dtype != kBF16 || kind != kEpiSwiGLU || plan.cfg != kBigTileCfg || n0 % 256 != 0 || n0 >= N ||
+        plan.tiles_n != n0 / 256)
+      return hipErrorInvalidValue;
+    GemmPlan pm = plan;
+    pm.n_main = 0;
+    hipError_t err = run_kind<bf16_t>(kind, pm, A, lda, W, wkb, M, n0, K, part, ea, s);
+    if (err != hipSuccess) return err;
+    double c;
+    const GemmPlan pt = plan_small(dtype, M, N - n0, K, kind, &c);
+    EpiArgs et = ea;  // units n0 / 2 .. of Z: same rows, Z offset by n0 / 2 columns
+    et.ldz = ea.ldz ? ea.ldz : ea.f;
+    et.out = (bf16_t *)ea.out + n0 / 2;
+    et.f = ea.f - n0 / 2;
+    const char *wt = (const char *)W + (size_t)(n0 / 32) * wkb * 1024;  // weight column blocks n0 / 32 ..
+    return run_kind<bf16_t>(kind, pt, A, lda, wt, wkb, M, N - n0, K, part, et, s);
+  }
   if (dtype == kF32) return run_kind<float>(kind, plan, A, lda, W, wkb, M, N, K, part, ea, s);
   return run_kind<bf16_t>(kind, plan, A, lda, W, wkb, M, N, K, part, ea, s);
 }

@@ -32,6 +32,7 @@ struct EpiArgs {
   int ld_src;
   int ldo;
   int f;
+  int ldz;  // kEpiSwiGLU: row stride of Z in elements (0: f)
   // kEpiQKV only: `bias` (d_q + 2 d_kv values of T, nullptr for none) is added after the RMSNorm row
   // scale; then, when rope_log2_theta > 0, q and k get the rotary embedding at the row's token index
   // (dims 2j, 2j + 1 of a head rotate by pos * theta^(-2j / hd); rope_log2_theta = log2 theta).
@@ -64,6 +65,9 @@ struct GemmPlan {
   int tiles_m, tiles_n;
   int splits;    // > 1: fp32 partials + a reduce kernel that applies the epilogue
   int k_split;   // K elements per split (multiple of the K slab)
+  // kEpiSwiGLU on the 256 x 256 kernel: columns [0, n_main) run as whole rounds of its tiles, the
+  // remaining columns as a second launch on the best smaller tile (0: one launch over all columns)
+  int n_main;
 };
 
 // Tile configuration of the large-M kernel: bf16 only, 256 x 256 tiles, never split, no kEpiPartial.

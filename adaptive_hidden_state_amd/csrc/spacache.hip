@@ -218,7 +218,7 @@ int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w
 }
 
 // number of kernels launch_gemm enqueues for a plan (the GEMM, plus the split-K reduce)
-int gemm_kernels(const GemmPlan &p) { return p.splits > 1 ? 2 : 1; }
+int gemm_kernels(const GemmPlan &p) { return p.splits > 1 || p.n_main > 0 ? 2 : 1; }
 
 // Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N). The 1 / rms
 // of every row of h_in must already be in the workspace (run_identify or launch_row_rinv).

@@ -2,7 +2,8 @@
 // HIP call): over a sweep of shapes, every plan must cover the output with its tiles and K with its
 // splits, keep split-K within the partial workspace bound, and pick only kernels valid for the
 // shape (the LDS-DMA and 256 x 256 kernels: bf16, no partial-only output; split-K never for the
-// SwiGLU or QKV epilogues, whose RMSNorm needs all of K).
+// SwiGLU or QKV epilogues, whose RMSNorm needs all of K; a column split only for SwiGLU on whole
+// rounds of 256 x 256 tiles).
 #include <stdio.h>
 
 #include "../adaptive_hidden_state_amd/csrc/gemm.hip"
@@ -22,7 +23,7 @@ int main() {
                            513, 700, 1000, 1024, 1030, 2048, 2624, 4096, 5248, 8192, 32768};
   static const int Ns[] = {16, 32, 64, 96, 128, 192, 256, 512, 1376, 2048, 3584, 4096, 4608, 12288, 24576, 37888};
   static const int Ks[] = {64, 128, 256, 512, 704, 1024, 3584, 4096, 12288, 18944};
-  long long plans = 0;
+  long long plans = 0, splits_n = 0;
   for (int dtype : {kBF16, kF32})
     for (int kind = 0; kind < 5; ++kind)
       for (int M : Ms)
@@ -32,6 +33,7 @@ int main() {
             if (K % slab != 0) continue;
             const GemmPlan p = plan_gemm(dtype, M, N, K, kind);
             ++plans;
+            if (p.n_main != 0) ++splits_n;
             const bool big = p.cfg == kBigTileCfg, dma = p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount;
             int bm = 0, bn = 0;
             if (big) {
@@ -47,8 +49,14 @@ int main() {
               continue;
             }
             if (p.bm != bm || p.bn != bn) fail("tile size does not match the configuration", dtype, M, N, K, kind, p);
-            if (p.tiles_m != (M + bm - 1) / bm || p.tiles_n != (N + bn - 1) / bn)
+            if (p.n_main != 0) {  // SwiGLU: whole rounds of 256 x 256 tiles over n_main columns, then the rest
+              if (kind != kEpiSwiGLU || dtype != kBF16 || !big || p.n_main % 256 != 0 || p.n_main <= 0 ||
+                  p.n_main >= N || p.tiles_n != p.n_main / 256 ||
+                  (long long)p.tiles_m * p.tiles_n > (long long)p.tiles_m * ((N + 255) / 256) / 256 * 256)
+                fail("bad column split", dtype, M, N, K, kind, p);
+            } else if (p.tiles_m != (M + bm - 1) / bm || p.tiles_n != (N + bn - 1) / bn) {
               fail("tiles do not cover the output", dtype, M, N, K, kind, p);
+            }
             if (p.splits < 1 || p.k_split <= 0 || p.k_split % slab != 0)
               fail("bad K split", dtype, M, N, K, kind, p);
             else if ((long long)p.splits * p.k_split < K || (long long)(p.splits - 1) * p.k_split >= K)
@@ -66,6 +74,6 @@ int main() {
                 gemm_partial_bytes(p, M, N) > gemm_partial_bound(M, N))
               fail("partials exceed the workspace bound", dtype, M, N, K, kind, p);
           }
-  printf("%lld plans checked, %d failures\n", plans, failures);
+  printf("%lld plans checked (%lld with a column split), %d failures\n", plans, splits_n, failures);
   return failures == 0 ? 0 : 1;
 }

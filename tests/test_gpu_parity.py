@@ -526,10 +526,12 @@ def test_dream_layer_step_full_size(dream_case):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("k", [102, 311])
+@pytest.mark.parametrize("k", [102, 311, 428])
 def test_dream_layer_step_full_size_stack_rows(dream_case, k):
-    """Row counts of other Dream stack layers (first layer k = 102; k = 311 on the way to the peak),
-    where the GEMMs take the 64-row register-path tiles with two to four workgroups per CU."""
+    """Row counts of other Dream stack layers (first layer k = 102; k = 311 and 428 on the way to the
+    peak): at 102 and 311 the GEMMs take the 64-row register-path tiles with two to four workgroups per
+    CU; at 428 (as at the peak, 512) gate/up runs one round of 256 x 256 tiles over its first 32768
+    columns and the remaining 5120 on a smaller tile."""
     _check_step(dream_case, k)
 
 
