@@ -111,10 +111,11 @@ hipError_t launch_row_rinv(int dtype, const void *x, int rows, int d, float eps,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Top-k least similar: one 1024-thread workgroup per sequence, keys held in registers
+// Top-k least similar: one 512-thread workgroup per sequence, keys held in registers (up to 32 per
+// thread: n <= 16384). 512 threads measured faster than 256 or 1024 at every n from 1024 to 8192
+// (fewer keys per thread than 256, fewer waves to synchronise than 1024).
 // ---------------------------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkPerThread = 16;  // n <= 16384
+constexpr int kTopkThreads = 512;
 
 // Unsigned key with the float order of s: NaN lowest, -0 equal to +0.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -310,15 +311,16 @@ __device__ void topk_block(const float *s, int n, int k, int32_t *out, TopkShare
     if (((sel >> j) & 1ull) && pos < (uint32_t)k) out[pos++] = start + j;
 }
 
+template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores, int n, int k,
                                                             int32_t *__restrict__ idx_out) {
   __shared__ TopkShared sh;
   const int b = blockIdx.x;
-  topk_block<kTopkThreads, kTopkPerThread>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
+  topk_block<kTopkThreads, PER>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
 }
 
 // The cosine pass fused with the Top-k of each sequence (n tokens per sequence, k of them selected):
-// every workgroup scores four tokens as proxy_cosine_kernel, then adds the number of its tokens in each
+// every workgroup scores eight tokens as proxy_cosine_kernel, then adds the number of its tokens in each
 // sequence to that sequence's counter; the workgroup whose addition completes a sequence runs the
 // Top-k of that sequence (topk_block, 256 threads) and resets its counter to 0. The scores cross
 // workgroups through agent-scope atomic stores and loads, which are coherent across the XCDs' L2
@@ -328,37 +330,39 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
 // loads are issued only after that addition returned the completing count. The counters must be 0 at
 // launch (the proxy projection that precedes this kernel clears them).
 template <int PER>
-__global__ __launch_bounds__(256) void cosine_topk_kernel(const float *__restrict__ part, int splits, int rows,
-                                                          int r, const float *pc_read, float *pc_write,
-                                                          float *__restrict__ p_out, float *scores,
-                                                          const float *__restrict__ ss_part, int d, float eps,
-                                                          float *__restrict__ rinv, int n, int k,
-                                                          int32_t *__restrict__ idx_out, uint32_t *counters) {
+__global__ __launch_bounds__(kTopkThreads) void cosine_topk_kernel(const float *__restrict__ part, int splits,
+                                                                   int rows, int r, const float *pc_read,
+                                                                   float *pc_write, float *__restrict__ p_out,
+                                                                   float *scores, const float *__restrict__ ss_part,
+                                                                   int d, float eps, float *__restrict__ rinv, int n,
+                                                                   int k, int32_t *__restrict__ idx_out,
+                                                                   uint32_t *counters) {
+  constexpr int RW = kTopkThreads / 64;  // rows (one per wave) of a workgroup
   __shared__ TopkShared sh;
-  __shared__ uint32_t last[4];
-  const int tid = threadIdx.x, row0 = blockIdx.x * 4;
+  __shared__ uint32_t last[RW];
+  const int tid = threadIdx.x, row0 = blockIdx.x * RW;
   const int row = row0 + (tid >> 6);
   if (row < rows) cosine_row<true>(part, splits, rows, r, row, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's memory operations (its score store included) completed
   __syncthreads();
-  if (tid == 0) {  // the (at most four) sequences of this workgroup's rows, in order
+  if (tid == 0) {  // the (at most RW) sequences of this workgroup's rows, in order
     int nl = 0;
-    for (int rr = row0; rr < min(row0 + 4, rows);) {
+    for (int rr = row0; rr < min(row0 + RW, rows);) {
       const int b = rr / n;
-      const int end = min(min(row0 + 4, rows), (b + 1) * n);
+      const int end = min(min(row0 + RW, rows), (b + 1) * n);
       const uint32_t cnt = (uint32_t)(end - rr);
       const uint32_t before = __hip_atomic_fetch_add(&counters[b], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (before + cnt == (uint32_t)n) last[nl++] = (uint32_t)b;
       rr = end;
     }
-    for (int j = nl; j < 4; ++j) last[j] = 0xffffffffu;
+    for (int j = nl; j < RW; ++j) last[j] = 0xffffffffu;
   }
   __syncthreads();
 #pragma unroll 1
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < RW; ++j) {
     const uint32_t b = last[j];  // uniform
     if (b == 0xffffffffu) break;
-    topk_block<256, PER, true>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
+    topk_block<kTopkThreads, PER, true>(scores + (size_t)b * n, n, k, idx_out + (size_t)b * k, sh);
     if (tid == 0) __hip_atomic_store(&counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();  // the shared state is reused by the next sequence
   }
@@ -369,23 +373,38 @@ hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, i
                               float *rinv, int k, int32_t *idx_out, uint32_t *counters, hipStream_t s) {
   const int rows = batch * n;
   if (rows <= 0) return hipSuccess;
-  if (n > 64 * 256 || k <= 0 || pc_read == nullptr || scores == nullptr) return hipErrorInvalidValue;
-  const dim3 grid((rows + 3) / 4), block(256);
-  if (n <= 4 * 256)
-    hipLaunchKernelGGL(cosine_topk_kernel<4>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
-                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
-  else if (n <= 16 * 256)
-    hipLaunchKernelGGL(cosine_topk_kernel<16>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
-                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
+  if (n > 32 * kTopkThreads || k <= 0 || pc_read == nullptr || scores == nullptr) return hipErrorInvalidValue;
+  constexpr int RW = kTopkThreads / 64;
+  const dim3 grid((rows + RW - 1) / RW), block(kTopkThreads);
+#define SPA_COSINE_TOPK(PER)                                                                                     \
+  hipLaunchKernelGGL(cosine_topk_kernel<PER>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out, \
+                     scores, ss_part, d, eps, rinv, n, k, idx_out, counters)
+  if (n <= 2 * kTopkThreads)
+    SPA_COSINE_TOPK(2);
+  else if (n <= 4 * kTopkThreads)
+    SPA_COSINE_TOPK(4);
+  else if (n <= 8 * kTopkThreads)
+    SPA_COSINE_TOPK(8);
+  else if (n <= 16 * kTopkThreads)
+    SPA_COSINE_TOPK(16);
   else
-    hipLaunchKernelGGL(cosine_topk_kernel<64>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
-                       scores, ss_part, d, eps, rinv, n, k, idx_out, counters);
+    SPA_COSINE_TOPK(32);
+#undef SPA_COSINE_TOPK
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s) {
   if (batch <= 0 || k <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(batch), dim3(kTopkThreads), 0, s, scores, n, k, idx_out);
+  if (n > 32 * kTopkThreads) return hipErrorInvalidValue;
+  const dim3 grid(batch), block(kTopkThreads);
+  if (n <= 4 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, scores, n, k, idx_out);
+  else if (n <= 8 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, scores, n, k, idx_out);
+  else if (n <= 16 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, scores, n, k, idx_out);
+  else
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, scores, n, k, idx_out);
   return hipGetLastError();
 }
 

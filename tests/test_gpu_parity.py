@@ -216,11 +216,13 @@ def test_topk_bit_exact(b, n):
 @pytest.mark.parametrize("shape", [SMALL_BF16[0], SMALL_BF16[1],
                                    synth.LayerShape(5, 3, 128, 2, 2, 64, 256, 16, "bf16"),
                                    synth.LayerShape(3, 1030, 256, 4, 4, 64, 688, 32, "bf16"),
+                                   synth.LayerShape(2, 3000, 256, 4, 4, 64, 688, 32, "bf16"),
                                    synth.LayerShape(1, 4100, 256, 4, 4, 64, 688, 32, "bf16")])
 def test_layer_step_fused_topk_equals_spa_topk(shape):
     """The Top-k taken inside the cosine kernel of spa_layer_step (by the workgroup that completes each
     sequence) equals spa_topk on the scores that step returns, and the oracle's selection on them:
-    sequences whose tokens share workgroups (N % 4 != 0, N < 4), and the three key-per-thread sizes."""
+    sequences whose tokens share workgroups (N % 8 != 0, N < 8), and the four key-per-thread sizes of
+    the fused path (2, 4, 8, 16 keys per thread: N up to 1024, 2048, 4096, 8192)."""
     import torch
     spa = _lib()
     s = shape
