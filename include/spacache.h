@@ -164,7 +164,8 @@ int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa
  * sequence, its Top-k; up to 8192 rows B N, beyond that proxy_cosine then topk; proxy_cosine alone
  * when k = 0), [proxy_copy_selected], qkv_gemm_scatter,
  * attention, wo_gemm_residual, gate_up_gemm_swiglu, down_gemm_scatter (a GEMM that splits K adds a
- * second kernel, its reduce, under the same name). */
+ * second kernel, its reduce, under the same name; so does a gate/up product split into whole rounds of
+ * 256 x 256 tiles and a remainder of columns). */
 typedef struct {
   hipEvent_t *marks;
   int32_t capacity;
