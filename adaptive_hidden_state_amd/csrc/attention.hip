@@ -681,33 +681,44 @@ static hipError_t launch_qg(const void *q, const void *kc, const void *vc, void 
   return hipGetLastError();
 }
 
-template <typename T, int HD>
-static hipError_t run_attention(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
-                                int n_tok, int hq, int hkv, hipStream_t s) {
+AttnPlan plan_attention(int dtype, int batch, int m_per_seq, int n_tok, int hq, int hkv, int hd) {
+  (void)n_tok;
+  (void)hkv;
+  (void)hd;
   constexpr int kCUs = 256;
   const long long heads = (long long)hq * batch;
-  if constexpr (sizeof(T) == 2) {
+  if (dtype == kBF16) {
     // The 256-query kernel once it fills the chip and its query blocks are at least 3/4 full: measured
     // at B = 8, N = 4096, 32 heads, 1024 and 656 queries per sequence 0.84 and 0.91 of the time of the
-    // kernel below, at 328 queries (blocks 64% full) 1.08.
+    // kernels below, at 328 queries (blocks 64% full) 1.08.
     const long long qb256 = (m_per_seq + 255) / 256;
-    if (heads * qb256 >= kCUs && 4LL * m_per_seq >= 3LL * 256 * qb256)
-      return launch_wide<HD>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+    if (heads * qb256 >= kCUs && 4LL * m_per_seq >= 3LL * 256 * qb256) return AttnPlan{kAttnWide};
   }
   const long long wg64 = heads * ((m_per_seq + 63) / 64), wg32 = heads * ((m_per_seq + 31) / 32);
-  if (wg64 < kCUs && wg32 <= kCUs) return launch_qg<T, HD, 1>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
-  return launch_qg<T, HD, 2>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  if (wg64 < kCUs && wg32 <= kCUs) return AttnPlan{kAttnQG1};
+  return AttnPlan{kAttnQG2};
 }
 
-hipError_t launch_attention(int dtype, const void *q, const void *kc, const void *vc, void *o, int batch,
-                            int m_per_seq, int n_tok, int hq, int hkv, int hd, hipStream_t s) {
+template <typename T, int HD>
+static hipError_t run_attention(const AttnPlan &p, const void *q, const void *kc, const void *vc, void *o, int batch,
+                                int m_per_seq, int n_tok, int hq, int hkv, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (p.kind == kAttnWide) return launch_wide<HD>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  }
+  if (p.kind == kAttnQG1) return launch_qg<T, HD, 1>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  if (p.kind == kAttnQG2) return launch_qg<T, HD, 2>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *kc, const void *vc, void *o,
+                            int batch, int m_per_seq, int n_tok, int hq, int hkv, int hd, hipStream_t s) {
   if (m_per_seq <= 0 || batch <= 0) return hipSuccess;
   if (dtype == kBF16) {
-    if (hd == 128) return run_attention<bf16_t, 128>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
-    return run_attention<bf16_t, 64>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+    if (hd == 128) return run_attention<bf16_t, 128>(plan, q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+    return run_attention<bf16_t, 64>(plan, q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
   }
-  if (hd == 128) return run_attention<float, 128>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
-  return run_attention<float, 64>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  if (hd == 128) return run_attention<float, 128>(plan, q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+  return run_attention<float, 64>(plan, q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
 }
 
 }  // namespace spa

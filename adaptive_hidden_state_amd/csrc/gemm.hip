@@ -1162,6 +1162,11 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
   return best;
 }
 
+GemmPlan gemm_tail_plan(int dtype, int M, int N, int K, int kind, const GemmPlan &p) {
+  double c;
+  return plan_small(dtype, M, N - p.n_main, K, kind, &c);
+}
+
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N) {
   return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -1253,8 +1258,7 @@ hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A,
     pm.n_main = 0;
     hipError_t err = run_kind<bf16_t>(kind, pm, A, lda, W, wkb, M, n0, K, part, ea, s);
     if (err != hipSuccess) return err;
-    double c;
-    const GemmPlan pt = plan_small(dtype, M, N - n0, K, kind, &c);
+    const GemmPlan pt = gemm_tail_plan(dtype, M, N, K, kind, plan);
     EpiArgs et = ea;  // units n0 / 2 .. of Z: same rows, Z offset by n0 / 2 columns
     et.ldz = ea.ldz ? ea.ldz : ea.f;
     et.out = (bf16_t *)ea.out + n0 / 2;

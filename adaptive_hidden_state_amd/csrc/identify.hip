@@ -139,7 +139,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return (uint32_t)x;
 }
 
-// Exclusive prefix sum over the workgroup (1024 threads = 16 waves); wsum holds 16 entries.
+// Exclusive prefix sum over the workgroup (kTopkThreads = 512 threads, 8 waves; wsum has room for up
+// to 16 waves).
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
@@ -322,9 +323,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
 // The cosine pass fused with the Top-k of each sequence (n tokens per sequence, k of them selected):
 // every workgroup scores eight tokens as proxy_cosine_kernel, then adds the number of its tokens in each
 // sequence to that sequence's counter; the workgroup whose addition completes a sequence runs the
-// Top-k of that sequence (topk_block, 256 threads) and resets its counter to 0. The scores cross
-// workgroups through agent-scope atomic stores and loads, which are coherent across the XCDs' L2
-// caches without cache-wide write-backs or invalidations (release / acquire fences would flush the
+// Top-k of that sequence (topk_block with all kTopkThreads = 512 threads) and resets its counter to
+// 0. The scores cross workgroups through agent-scope atomic stores and loads, which are coherent
+// across the XCDs' L2 caches without cache-wide write-backs or invalidations (release / acquire fences would flush the
 // whole L2, including this kernel's P^c writes); each wave waits until its score store has completed
 // before the workgroup's counter addition, which is itself an agent-scope atomic, and the Top-k's
 // loads are issued only after that addition returned the completing count. The counters must be 0 at
@@ -391,6 +392,12 @@ hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, i
     SPA_COSINE_TOPK(32);
 #undef SPA_COSINE_TOPK
   return hipGetLastError();
+}
+
+int topk_keys_per_thread(int n, bool fused) {
+  for (int per = fused ? 2 : 4; per < 32; per *= 2)
+    if (n <= per * kTopkThreads) return per;
+  return 32;
 }
 
 hipError_t launch_topk(const float *scores, int batch, int n, int k, int32_t *idx_out, hipStream_t s) {

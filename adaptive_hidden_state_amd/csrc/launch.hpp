@@ -79,6 +79,9 @@ constexpr int kDmaTileCount = 3;
 constexpr int kDmaTiles[kDmaTileCount][2] = {{128, 192}, {128, 128}, {128, 64}};
 
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
+// Plan of the columns [p.n_main, N) of a column-split SwiGLU plan (p.n_main > 0), launched after the
+// whole rounds of 256 x 256 tiles.
+GemmPlan gemm_tail_plan(int dtype, int M, int N, int K, int kind, const GemmPlan &p);
 size_t gemm_partial_bytes(const GemmPlan &p, int M, int N);
 
 // A: M x K row-major (lda elements per row). W: fragment-packed (see below), wkb = packed blocks per
@@ -116,6 +119,11 @@ hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const voi
                               void *dst, hipStream_t s);
 
 // Phase 1 pieces.
+// Up to this many hidden rows (B N) the Top-k runs inside the cosine kernel (launch_cosine_topk);
+// beyond it the cosine kernel and the Top-k kernel run one after the other.
+constexpr int kFusedTopkRows = 8192;
+// Keys held per thread by the Top-k of an n-token sequence (fused: inside the cosine kernel).
+int topk_keys_per_thread(int n, bool fused);
 // ss_part (splits x rows, nullable): the proxy GEMM's per-split sums of squares of each hidden row;
 // with rinv set, rinv[row] = 1 / sqrt(sum / d + eps) is written as well.
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,
@@ -134,7 +142,14 @@ hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *id
                                 int k, int r, hipStream_t s);
 
 // Sparse-query attention: q (B*m_per_seq x hq*hd) against K^c/V^c (B x hkv x n_tok x hd).
-hipError_t launch_attention(int dtype, const void *q, const void *kc, const void *vc, void *o, int batch,
-                            int m_per_seq, int n_tok, int hq, int hkv, int hd, hipStream_t s);
+// The kernel that serves a launch is chosen on the host: kAttnQG1 / kAttnQG2 = workgroups of 32 / 64
+// queries of one head with the keys split over the waves; kAttnWide = 256 queries of one head (bf16).
+enum AttnKind { kAttnQG1 = 0, kAttnQG2 = 1, kAttnWide = 2 };
+struct AttnPlan {
+  int kind;
+};
+AttnPlan plan_attention(int dtype, int batch, int m_per_seq, int n_tok, int hq, int hkv, int hd);
+hipError_t launch_attention(int dtype, const AttnPlan &plan, const void *q, const void *kc, const void *vc, void *o,
+                            int batch, int m_per_seq, int n_tok, int hq, int hkv, int hd, hipStream_t s);
 
 }  // namespace spa

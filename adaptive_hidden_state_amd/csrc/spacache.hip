@@ -5,8 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "launch.hpp"
 #include "spacache.h"
+#include "step_plan.hpp"
 
 using namespace spa;
 
@@ -68,6 +68,8 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+StepShape step_shape(const Dims &D) { return StepShape{D.dtype, D.B, D.N, D.d, D.hq, D.hkv, D.hd, D.F, D.r}; }
+
 // Workspace regions. Offsets are multiples of 256 bytes.
 struct Layout {
   GemmPlan proxy;
@@ -78,7 +80,7 @@ Layout make_layout(const Dims &D, int k_max) {
   Layout L{};
   const size_t rows = (size_t)D.B * D.N;
   const size_t m = (size_t)D.B * (size_t)k_max;
-  L.proxy = plan_gemm(D.dtype, (int)rows, D.r, D.d, kEpiPartial);
+  L.proxy = plan_step(step_shape(D), 0, false).proxy;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -169,6 +171,58 @@ int check_cache(const spa_layer_cache *c, const Dims &D, const void *h_in) {
   return SPA_OK;
 }
 
+// A device buffer as (pointer, bytes) for the overlap checks; null pointers and empty spans overlap
+// nothing.
+struct Span {
+  const void *p;
+  size_t n;
+};
+
+bool spans_overlap(const Span &a, const Span &b) {
+  return a.p != nullptr && b.p != nullptr && a.n > 0 && b.n > 0 && overlap(a.p, a.n, b.p, b.n);
+}
+
+// SPA_ERR_ALIAS unless the buffers a call writes are pairwise disjoint and disjoint from every buffer
+// it only reads.
+int check_disjoint(const Span *written, int nw, const Span *read, int nr) {
+  for (int i = 0; i < nw; ++i) {
+    for (int j = i + 1; j < nw; ++j)
+      if (spans_overlap(written[i], written[j])) return SPA_ERR_ALIAS;
+    for (int j = 0; j < nr; ++j)
+      if (spans_overlap(written[i], read[j])) return SPA_ERR_ALIAS;
+  }
+  return SPA_OK;
+}
+
+size_t packed_bytes(const Dims &D, int rows, int cols, int kind) {
+  int rp, cp;
+  packed_dims(kind, rows, cols, &rp, &cp);
+  return (size_t)rp * cp * D.e;
+}
+
+// The read-only inputs of a layer call: h_in and the packed weights (and the optional q/k/v biases).
+int read_spans(const Dims &D, const spa_layer_weights *w, const void *h_in, Span *out) {
+  const int nqkv = D.dq + 2 * D.dkv;
+  out[0] = Span{h_in, (size_t)D.B * D.N * D.d * D.e};
+  out[1] = Span{w->w_r, packed_bytes(D, D.r, D.d, kPackPlain)};
+  out[2] = Span{w->w_qkv, packed_bytes(D, nqkv, D.d, kPackPlain)};
+  out[3] = Span{w->w_o, packed_bytes(D, D.d, D.dq, kPackPlain)};
+  out[4] = Span{w->w_gate_up, packed_bytes(D, 2 * D.F, D.d, kPackGateUp)};
+  out[5] = Span{w->w_down, packed_bytes(D, D.d, D.F, kPackPlain)};
+  out[6] = Span{w->b_qkv, (size_t)nqkv * D.e};
+  return 7;
+}
+
+// The caches a layer call writes: K^c, V^c, H^c and P^c.
+int cache_spans(const Dims &D, const spa_layer_cache *c, Span *out) {
+  const size_t kvb = (size_t)D.B * D.hkv * D.N * D.hd * D.e;
+  out[0] = Span{c->k_cache, kvb};
+  out[1] = Span{c->v_cache, kvb};
+  out[2] = Span{c->h_cache, (size_t)D.B * D.N * D.d * D.e};
+  out[3] = Span{c->p_cache, (size_t)D.B * D.N * D.r * 4};
+  return 4;
+}
+
 int check_ws(void *ws, size_t ws_bytes, size_t need) {
   if (need > ws_bytes) return SPA_ERR_WORKSPACE;
   if (need > 0 && ws == nullptr) return SPA_ERR_WORKSPACE;
@@ -176,22 +230,20 @@ int check_ws(void *ws, size_t ws_bytes, size_t need) {
   return SPA_OK;
 }
 
-// Phase 1 on device: proxy GEMM (fp32 split-K partials) then reduce + cosine + writes.
-// Phase 1. With k > 0 (and pc_read, scores set) the Top-k of every sequence is taken too (idx_out,
-// B x k): up to kFusedTopkRows hidden rows inside the cosine kernel, beyond that (where the waiting of
-// every wave for its stores before the counter update, repeated over many rounds of waves, costs more
-// than the separate launch saves; measured at 32768 rows) by the Top-k kernel after it. With k = 0
-// only the scores.
-constexpr int kFusedTopkRows = 8192;
-
-int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w_r, const float *pc_read,
-                 float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s, Marks &mk, int k = 0,
-                 int32_t *idx_out = nullptr) {
+// Phase 1 on device: proxy GEMM (fp32 split-K partials) then reduce + cosine + writes. With plan
+// kIdFusedTopk / kIdSeparateTopk (k > 0, pc_read and scores set) the Top-k of every sequence is taken
+// too (idx_out, B x k): up to kFusedTopkRows hidden rows inside the cosine kernel, beyond that (where
+// the waiting of every wave for its stores before the counter update, repeated over many rounds of
+// waves, costs more than the separate launch saves; measured at 32768 rows) by the Top-k kernel after
+// it. kIdScores: only the scores.
+int run_identify(const Dims &D, const Layout &L, const StepPlan &P, const void *h_in, const void *w_r,
+                 const float *pc_read, float *pc_write, float *p_out, float *scores, void *ws, hipStream_t s,
+                 Marks &mk, int k = 0, int32_t *idx_out = nullptr) {
   const int rows = D.B * D.N;
   float *part = (float *)at(ws, L.ppart);
   float *ssp = (float *)at(ws, L.ssp), *rinv = (float *)at(ws, L.rinv);
   uint32_t *counters = (uint32_t *)at(ws, L.counters);
-  const bool topk = k > 0 && rows <= kFusedTopkRows;
+  const bool topk = P.identify == kIdFusedTopk;
   EpiArgs ea{};
   ea.ss_out = ssp;  // the projection streams every hidden row: it also sums their squares
   if (topk) {       // and clears the Top-k counters of the cosine kernel that follows
@@ -209,7 +261,7 @@ int run_identify(const Dims &D, const Layout &L, const void *h_in, const void *w
     SPA_TRY(launch_proxy_cosine(part, L.proxy.splits, rows, D.r, pc_read, pc_write, p_out, scores, ssp, D.d, D.eps,
                                 rinv, s));
     SPA_TRY(mk.mark("proxy_cosine"));
-    if (k > 0) {
+    if (P.identify == kIdSeparateTopk) {
       SPA_TRY(launch_topk(scores, D.B, D.N, k, idx_out, s));
       SPA_TRY(mk.mark("topk"));
     }
@@ -222,9 +274,10 @@ int gemm_kernels(const GemmPlan &p) { return p.splits > 1 || p.n_main > 0 ? 2 : 
 
 // Phases 2 and 3 for update sets idx (B x k_per_seq; nullptr = every token, k_per_seq = N). The 1 / rms
 // of every row of h_in must already be in the workspace (run_identify or launch_row_rinv).
-int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const spa_layer_cache *c,
-               const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s, Marks &mk) {
-  const int M = D.B * k_per_seq;
+int run_sparse(const Dims &D, const Layout &L, const StepPlan &P, const spa_layer_weights *w,
+               const spa_layer_cache *c, const void *h_in, const int32_t *idx, int k_per_seq, void *ws, hipStream_t s,
+               Marks &mk) {
+  const int M = P.M;
   if (M == 0) return SPA_OK;
   void *q = at(ws, L.q), *o = at(ws, L.o), *y = at(ws, L.y), *z = at(ws, L.z);
   float *gpart = (float *)at(ws, L.gpart), *ss32 = (float *)at(ws, L.ss32);
@@ -247,12 +300,13 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   qkv.rope_log2_theta = D.rope_log2;
   qkv.row_rinv = (const float *)at(ws, L.rinv);
   const int nqkv = D.dq + 2 * D.dkv;
-  const GemmPlan p_qkv = plan_gemm(D.dtype, M, nqkv, D.d, kEpiQKV);
+  const GemmPlan &p_qkv = P.qkv;
   SPA_TRY(launch_gemm(D.dtype, kEpiQKV, p_qkv, h_in, D.d, w->w_qkv, packed_wkb(D.dtype, D.d), M, nqkv, D.d, gpart,
                       qkv, s));
   SPA_TRY(mk.mark("qkv_gemm_scatter", gemm_kernels(p_qkv)));
 
-  SPA_TRY(launch_attention(D.dtype, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd, s));
+  SPA_TRY(launch_attention(D.dtype, P.attn, q, c->k_cache, c->v_cache, o, D.B, k_per_seq, D.N, D.hq, D.hkv, D.hd,
+                           s));
   SPA_TRY(mk.mark("attention"));
 
   EpiArgs wo{};
@@ -264,7 +318,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   wo.ld_src = D.d;
   wo.ldo = D.d;
   wo.ss_out = ss32;  // statistics of y for the FFN RMSNorm
-  const GemmPlan p_wo = plan_gemm(D.dtype, M, D.d, D.dq, kEpiResid);
+  const GemmPlan &p_wo = P.wo;
   SPA_TRY(launch_gemm(D.dtype, kEpiResid, p_wo, o, D.dq, w->w_o, packed_wkb(D.dtype, D.dq), M, D.d, D.dq, gpart, wo,
                       s));
   SPA_TRY(mk.mark("wo_gemm_residual", gemm_kernels(p_wo)));
@@ -277,7 +331,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   gu.norm_eps = D.eps;
   gu.ss_in = ss32;
   gu.ss_n = D.d / 32;
-  const GemmPlan p_gu = plan_gemm(D.dtype, M, 2 * D.Fp, D.d, kEpiSwiGLU);
+  const GemmPlan &p_gu = P.gu;
   SPA_TRY(launch_gemm(D.dtype, kEpiSwiGLU, p_gu, y, D.d, w->w_gate_up, packed_wkb(D.dtype, D.d), M, 2 * D.Fp, D.d,
                       gpart, gu, s));
   SPA_TRY(mk.mark("gate_up_gemm_swiglu", gemm_kernels(p_gu)));
@@ -290,7 +344,7 @@ int run_sparse(const Dims &D, const Layout &L, const spa_layer_weights *w, const
   dn.n_tok = D.N;
   dn.ld_src = D.d;
   dn.ldo = D.d;
-  const GemmPlan p_dn = plan_gemm(D.dtype, M, D.d, D.Fp, kEpiResidScatter);
+  const GemmPlan &p_dn = P.dn;
   SPA_TRY(launch_gemm(D.dtype, kEpiResidScatter, p_dn, z, D.Fp, w->w_down, packed_wkb(D.dtype, D.F), M, D.d, D.Fp,
                       gpart, dn, s));
   SPA_TRY(mk.mark("down_gemm_scatter", gemm_kernels(p_dn)));
@@ -383,10 +437,17 @@ int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa
   if ((st = check_cache(cache, D, h_in)) != SPA_OK) return st;
   const Layout L = make_layout(D, D.N);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  {
+    Span wr[5], rd[7];
+    const int nw = cache_spans(D, cache, wr);
+    wr[nw] = Span{ws, L.total};
+    if ((st = check_disjoint(wr, nw + 1, rd, read_spans(D, w, h_in, rd))) != SPA_OK) return st;
+  }
+  const StepPlan P = plan_step(step_shape(D), D.N, false);
   Marks mk{nullptr, stream};
-  if ((st = run_identify(D, L, h_in, w->w_r, nullptr, cache->p_cache, nullptr, nullptr, ws, stream, mk)) != SPA_OK)
+  if ((st = run_identify(D, L, P, h_in, w->w_r, nullptr, cache->p_cache, nullptr, nullptr, ws, stream, mk)) != SPA_OK)
     return st;
-  return run_sparse(D, L, w, cache, h_in, nullptr, D.N, ws, stream, mk);
+  return run_sparse(D, L, P, w, cache, h_in, nullptr, D.N, ws, stream, mk);
 }
 
 int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
@@ -405,26 +466,31 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
   if (policy != SPA_PROXY_WRITE_ALL && policy != SPA_PROXY_WRITE_SELECTED) return SPA_ERR_INVALID_ARG;
   if (k > 0 && idx_out == nullptr) return SPA_ERR_INVALID_ARG;
   if ((idx_out && !aligned16(idx_out)) || (scores_out && !aligned16(scores_out))) return SPA_ERR_ALIGN;
-  const size_t xb = (size_t)D.B * D.N * D.d * D.e;
-  if (idx_out && (overlap(idx_out, (size_t)D.B * k * 4, h_in, xb) ||
-                  overlap(idx_out, (size_t)D.B * k * 4, cache->p_cache, (size_t)D.B * D.N * D.r * 4)))
-    return SPA_ERR_ALIAS;
   const Layout L = make_layout(D, k);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  {
+    Span wr[7], rd[7];
+    int nw = cache_spans(D, cache, wr);
+    wr[nw++] = Span{idx_out, (size_t)D.B * k * 4};
+    wr[nw++] = Span{scores_out, (size_t)D.B * D.N * 4};
+    wr[nw++] = Span{ws, L.total};
+    if ((st = check_disjoint(wr, nw, rd, read_spans(D, w, h_in, rd))) != SPA_OK) return st;
+  }
   float *scores = scores_out ? scores_out : (float *)at(ws, L.scores);
   const bool sel = policy == SPA_PROXY_WRITE_SELECTED;
   float *pbuf = (float *)at(ws, L.pbuf);
+  const StepPlan P = plan_step(step_shape(D), k, true);
   Marks mk{timing, stream};
   SPA_TRY(mk.mark("start"));
-  if ((st = run_identify(D, L, h_in, w->w_r, cache->p_cache, sel ? nullptr : cache->p_cache, sel ? pbuf : nullptr,
-                         scores, ws, stream, mk, k, idx_out)) != SPA_OK)
+  if ((st = run_identify(D, L, P, h_in, w->w_r, cache->p_cache, sel ? nullptr : cache->p_cache,
+                         sel ? pbuf : nullptr, scores, ws, stream, mk, k, idx_out)) != SPA_OK)
     return st;
   if (k == 0) return SPA_OK;
   if (sel) {
     SPA_TRY(launch_copy_selected(pbuf, cache->p_cache, idx_out, D.B, D.N, k, D.r, stream));
     SPA_TRY(mk.mark("proxy_copy_selected"));
   }
-  return run_sparse(D, L, w, cache, h_in, idx_out, k, ws, stream, mk);
+  return run_sparse(D, L, P, w, cache, h_in, idx_out, k, ws, stream, mk);
 }
 
 int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
@@ -445,11 +511,17 @@ int spa_identify(const spa_shape *shape, const void *h_in, const void *w_r, cons
       (scores_out && !aligned16(scores_out)))
     return SPA_ERR_ALIGN;
   const size_t pb = (size_t)D.B * D.N * D.r * 4;
-  if (p_out && p_cache && overlap(p_out, pb, p_cache, pb)) return SPA_ERR_ALIAS;
   const Layout L = make_layout(D, 0);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  {
+    const Span wr[3] = {{p_out, pb}, {scores_out, (size_t)D.B * D.N * 4}, {ws, L.total}};
+    const Span rd[3] = {{h_in, (size_t)D.B * D.N * D.d * D.e}, {w_r, packed_bytes(D, D.r, D.d, kPackPlain)},
+                        {p_cache, pb}};
+    if ((st = check_disjoint(wr, 3, rd, 3)) != SPA_OK) return st;
+  }
+  const StepPlan P = plan_step(step_shape(D), 0, false);
   Marks mk{nullptr, stream};
-  return run_identify(D, L, h_in, w_r, p_cache, nullptr, p_out, scores_out, ws, stream, mk);
+  return run_identify(D, L, P, h_in, w_r, p_cache, nullptr, p_out, scores_out, ws, stream, mk);
 }
 
 int spa_topk(int32_t batch, int32_t n, const float *scores, int32_t k, int32_t *idx_out, hipStream_t stream) {
@@ -457,6 +529,8 @@ int spa_topk(int32_t batch, int32_t n, const float *scores, int32_t k, int32_t *
   if (n > 16384) return SPA_ERR_UNSUPPORTED;
   if (scores == nullptr || (k > 0 && idx_out == nullptr)) return SPA_ERR_INVALID_ARG;
   if (!aligned16(scores) || (idx_out && !aligned16(idx_out))) return SPA_ERR_ALIGN;
+  const Span wr[1] = {{idx_out, (size_t)batch * k * 4}}, rd[1] = {{scores, (size_t)batch * n * 4}};
+  if (check_disjoint(wr, 1, rd, 1) != SPA_OK) return SPA_ERR_ALIAS;
   return hip_status(launch_topk(scores, batch, n, k, idx_out, stream));
 }
 
@@ -472,9 +546,18 @@ int spa_sparse_update(const spa_shape *shape, const spa_layer_weights *w, const 
   if (idx && !aligned16(idx)) return SPA_ERR_ALIGN;
   const Layout L = make_layout(D, k);
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
+  {
+    Span wr[5], rd[8];
+    const int nw = cache_spans(D, cache, wr) - 1;  // P^c is not touched
+    wr[nw] = Span{ws, L.total};
+    int nr = read_spans(D, w, h_in, rd);
+    rd[nr++] = Span{idx, (size_t)D.B * k * 4};
+    if ((st = check_disjoint(wr, nw + 1, rd, nr)) != SPA_OK) return st;
+  }
+  const StepPlan P = plan_step(step_shape(D), k, false);
   Marks mk{nullptr, stream};
   if (k > 0) SPA_TRY(launch_row_rinv(D.dtype, h_in, D.B * D.N, D.d, D.eps, (float *)at(ws, L.rinv), stream));
-  return run_sparse(D, L, w, cache, h_in, idx, k, ws, stream, mk);
+  return run_sparse(D, L, P, w, cache, h_in, idx, k, ws, stream, mk);
 }
 
 int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const void *k_cache, const void *v_cache,
@@ -489,8 +572,9 @@ int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const v
   const size_t kvb = (size_t)D.B * D.hkv * D.N * D.hd * D.e;
   if (overlap(o_out, ob, q, ob) || overlap(o_out, ob, k_cache, kvb) || overlap(o_out, ob, v_cache, kvb))
     return SPA_ERR_ALIAS;
+  const AttnPlan ap = plan_attention(D.dtype, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd);
   return hip_status(
-      launch_attention(D.dtype, q, k_cache, v_cache, o_out, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd, stream));
+      launch_attention(D.dtype, ap, q, k_cache, v_cache, o_out, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd, stream));
 }
 
 }  // extern "C"

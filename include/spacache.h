@@ -24,6 +24,10 @@
  *   - Errors. Every call validates its arguments before any launch and returns a spa_status;
  *     nothing aborts or throws. SPA_ERR_HIP reports a launch failure; faults inside kernels surface
  *     at the caller's next synchronisation.
+ *   - Aliasing. The buffers a call writes (the caches, idx_out, scores_out, p_out, o_out and the
+ *     workspace) must not overlap one another nor any buffer the call only reads (h_in, the packed
+ *     weights and biases, idx, the p_cache of spa_identify, the scores of spa_topk, q and K^c/V^c of
+ *     spa_attend): SPA_ERR_ALIAS otherwise. Read-only buffers may overlap each other.
  *   - Threads. No global mutable state: concurrent calls on different streams with disjoint
  *     buffers are safe.
  *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0, d <= 8192 (bf16) or 4096 (fp32);

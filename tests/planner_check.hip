@@ -1,12 +1,27 @@
-// Host-side check of the GEMM planner (built by tests/test_planner.py and run on the CPU; it makes no
-// HIP call): over a sweep of shapes, every plan must cover the output with its tiles and K with its
-// splits, keep split-K within the partial workspace bound, and pick only kernels valid for the
-// shape (the LDS-DMA and 256 x 256 kernels: bf16, no partial-only output; split-K never for the
+// Host-side checks of the kernel planners (built by the host tests with hipcc and run on the CPU; no
+// HIP call is made).
+//
+// With no argument: over a sweep of shapes, every GEMM plan must cover the output with its tiles and K
+// with its splits, keep split-K within the partial workspace bound, and pick only kernels valid for
+// the shape (the LDS-DMA and 256 x 256 kernels: bf16, no partial-only output; split-K never for the
 // SwiGLU or QKV epilogues, whose RMSNorm needs all of K; a column split only for SwiGLU on whole
 // rounds of 256 x 256 tiles).
+//
+// With "instances": reads lines "tag dtype B N d hq hkv hd F r k mode" from stdin (mode step: the
+// cached step with Top-k of k rows; full: the full recompute; identify: spa_identify; sparse:
+// spa_sparse_update of k rows; attend: spa_attend of k queries per sequence) and prints
+// "tag key key ...": one key per kernel instance the call runs (kernel and tile, split-K or not, one
+// or several column tiles, a ragged last row tile or not, and the variants of the identification and
+// attention kernels).
 #include <stdio.h>
+#include <string.h>
 
+#include <string>
+
+#include "../adaptive_hidden_state_amd/csrc/attention.hip"
 #include "../adaptive_hidden_state_amd/csrc/gemm.hip"
+#include "../adaptive_hidden_state_amd/csrc/identify.hip"
+#include "../adaptive_hidden_state_amd/csrc/step_plan.hpp"
 
 using namespace spa;
 
@@ -17,7 +32,7 @@ static void fail(const char *what, int dtype, int M, int N, int K, int kind, con
            dtype, M, N, K, kind, p.cfg, p.bm, p.bn, p.tiles_m, p.tiles_n, p.splits, p.k_split);
 }
 
-int main() {
+static int sweep() {
   static const int Ms[] = {1,   2,   3,   7,   16,  31,  32,  33,  51,  63,   64,   65,   87,   100,  127,
                            128, 129, 133, 191, 192, 193, 200, 255, 256, 257,  311,  383,  384,  428,  512,
                            513, 700, 1000, 1024, 1030, 2048, 2624, 4096, 5248, 8192, 32768};
@@ -76,4 +91,100 @@ int main() {
           }
   printf("%lld plans checked (%lld with a column split), %d failures\n", plans, splits_n, failures);
   return failures == 0 ? 0 : 1;
+}
+
+// ---------------------------------------------------------------------------------------------
+// instance keys
+// ---------------------------------------------------------------------------------------------
+static std::string tile_name(int dtype, const GemmPlan &p) {
+  char b[64];
+  if (p.cfg == kBigTileCfg)
+    snprintf(b, sizeof b, "big256x256");
+  else if (p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount)
+    snprintf(b, sizeof b, "dma%dx%d", p.bm, p.bn);
+  else
+    snprintf(b, sizeof b, "reg%dx%d%s", p.bm, p.bn, dtype == kF32 ? "f32" : "");
+  return b;
+}
+
+static std::string plan_key(int dtype, const GemmPlan &p, int M) {
+  std::string k = tile_name(dtype, p);
+  k += p.splits > 1 ? "/splitk" : "/nosplit";
+  k += p.tiles_n > 1 ? "/ncols" : "/1col";
+  k += M % p.bm != 0 ? "/ragged" : "/whole";
+  return k;
+}
+
+static std::string gemm_key(const char *op, int dtype, int M, int N, int K, int kind, const GemmPlan &p) {
+  std::string k = std::string(op) + ":" + plan_key(dtype, p, M);
+  if (p.n_main > 0) k += "+tail:" + plan_key(dtype, gemm_tail_plan(dtype, M, N, K, kind, p), M);
+  return k;
+}
+
+static std::string attn_key(const StepShape &s, int m, const AttnPlan &a) {
+  static const char *names[] = {"qg1", "qg2", "wide"};
+  static const int queries[] = {32, 64, 256};
+  char b[96];
+  snprintf(b, sizeof b, "attn:%s:%s:hd%d:%s:%s:%s", names[a.kind], s.dtype == kF32 ? "f32" : "bf16", s.hd,
+           s.hq != s.hkv ? "gqa" : "mha", m % queries[a.kind] ? "raggedq" : "wholeq",
+           s.N % 32 ? "raggedkeys" : "wholekeys");
+  return b;
+}
+
+static void print_sparse(const StepShape &s, const StepPlan &P, int k) {
+  const int dq = s.hq * s.hd, dkv = s.hkv * s.hd, fp = step_fpad(s);
+  printf(" %s", gemm_key("qkv", s.dtype, P.M, dq + 2 * dkv, s.d, kEpiQKV, P.qkv).c_str());
+  printf(" %s", attn_key(s, k, P.attn).c_str());
+  printf(" %s", gemm_key("wo", s.dtype, P.M, s.d, dq, kEpiResid, P.wo).c_str());
+  printf(" %s", gemm_key("gu", s.dtype, P.M, 2 * fp, s.d, kEpiSwiGLU, P.gu).c_str());
+  printf(" %s", gemm_key("dn", s.dtype, P.M, s.d, fp, kEpiResidScatter, P.dn).c_str());
+}
+
+static int instances() {
+  char line[512];
+  while (fgets(line, sizeof line, stdin)) {
+    char tag[256], dt[16], mode[32];
+    StepShape s{};
+    int k = 0;
+    if (sscanf(line, "%255s %15s %d %d %d %d %d %d %d %d %d %31s", tag, dt, &s.B, &s.N, &s.d, &s.hq, &s.hkv, &s.hd,
+               &s.F, &s.r, &k, mode) != 12) {
+      if (line[0] != '\n') printf("BAD %s", line);
+      continue;
+    }
+    s.dtype = strcmp(dt, "f32") == 0 ? kF32 : kBF16;
+    const bool step = strcmp(mode, "step") == 0, full = strcmp(mode, "full") == 0;
+    const bool identify = strcmp(mode, "identify") == 0, sparse = strcmp(mode, "sparse") == 0;
+    if (strcmp(mode, "attend") == 0) {
+      const AttnPlan a = plan_attention(s.dtype, s.B, k, s.N, s.hq, s.hkv, s.hd);
+      printf("%s %s\n", tag, k > 0 ? attn_key(s, k, a).c_str() : "");
+      continue;
+    }
+    if (!step && !full && !identify && !sparse) {
+      printf("BAD %s", line);
+      continue;
+    }
+    const int kk = full ? s.N : (identify ? 0 : k);
+    const StepPlan P = plan_step(s, kk, step);
+    printf("%s", tag);
+    if (!sparse) {
+      const int rows = s.B * s.N;
+      printf(" %s", gemm_key("proxy", s.dtype, rows, s.r, s.d, kEpiPartial, P.proxy).c_str());
+      const char *wide = s.r > 256 ? ":wide" : "";
+      if (P.identify == kIdFusedTopk)
+        printf(" cos+topk:per%d%s", topk_keys_per_thread(s.N, true), wide);
+      else
+        printf(" cos%s", wide);
+      if (P.identify == kIdSeparateTopk) printf(" topk:per%d", topk_keys_per_thread(s.N, false));
+    } else {
+      printf(" rinv");
+    }
+    if (P.M > 0) print_sparse(s, P, kk);
+    printf("\n");
+  }
+  return 0;
+}
+
+int main(int argc, char **argv) {
+  if (argc > 1 && strcmp(argv[1], "instances") == 0) return instances();
+  return sweep();
 }

@@ -223,3 +223,43 @@ def test_packed_weight_bytes(lib):
     assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x200008), _fake(0x100000), None) == -4  # scale
     assert lib.spa_pack_weight(1, 64, 64, 0, _fake(0x1000), _fake(0x100040), _fake(0x100000), None) == -3  # scale
     assert lib.spa_pack_weight(1, 64, 64, 0, None, None, _fake(0x100000), None) == -1
+
+
+def test_alias_checks_of_every_written_buffer(lib):
+    """Each buffer a call writes must be disjoint from the others it writes and from what it only
+    reads: outputs over the caches, the workspace, h_in or a weight are refused before any launch."""
+    s = _shape()
+    w, c = _weights(), _cache()
+    WS = 0xA0000000
+    ws_bytes = _ws_bytes(lib, s, 256)[1]
+    cache_base = 0x40000000
+    # spa_layer_step: idx_out / scores_out over H^c, K^c, over the workspace, over each other
+    assert _step(lib, s, w, c, X, idx=cache_base + 0x20000000) == -3           # idx_out inside H^c
+    assert _step(lib, s, w, c, X, scores=cache_base) == -3                       # scores_out inside K^c
+    assert _step(lib, s, w, c, X, scores=WS + 4096, ws_bytes=ws_bytes) == -3    # scores_out inside the workspace
+    assert _step(lib, s, w, c, X, idx=WS, ws_bytes=ws_bytes) == -3              # idx_out inside the workspace
+    assert _step(lib, s, w, c, X, idx=0x90000000, scores=0x90000000 + 512) == -3  # idx_out over scores_out
+    assert _step(lib, s, w, c, X, scores=X + 64) == -3                          # scores_out over h_in
+    assert _step(lib, s, w, c, X, idx=0x100000) == -3                           # idx_out over packed w_r
+    assert _step(lib, s, w, c, X, ws=cache_base + 0x30000000, ws_bytes=ws_bytes) == -3   # workspace over P^c
+    assert _step(lib, s, _weights(base=cache_base + 0x20000000), c, X) == -3   # a weight inside H^c
+    # spa_layer_full: the workspace over a cache
+    assert lib.spa_layer_full(ctypes.byref(s), ctypes.byref(w), ctypes.byref(c), _fake(X), _fake(cache_base),
+                              1 << 40, None) == -3
+    # spa_sparse_update: idx inside H^c (written), workspace over K^c
+    assert lib.spa_sparse_update(ctypes.byref(s), ctypes.byref(w), ctypes.byref(c), _fake(X),
+                                 _fake(cache_base + 0x20000000), 5, _fake(WS), 1 << 40, None) == -3
+    assert lib.spa_sparse_update(ctypes.byref(s), ctypes.byref(w), ctypes.byref(c), _fake(X), _fake(0x90000000), 5,
+                                 _fake(cache_base), 1 << 40, None) == -3
+    # spa_identify: scores_out over h_in, over the workspace, over p_out, p_out over w_r
+    P = 0xB0000000
+    ident = lambda pc, po, so, ws=WS: lib.spa_identify(ctypes.byref(s), _fake(X), _fake(P), _fake(pc) if pc else None,
+                                                       _fake(po) if po else None, _fake(so) if so else None,
+                                                       _fake(ws), 1 << 40, None)
+    assert ident(0xC0000000, None, X) == -3
+    assert ident(0xC0000000, None, WS) == -3
+    assert ident(0xC0000000, 0xD0000000, 0xD0000000 + 1024) == -3
+    assert ident(0xC0000000, P, 0xE0000000) == -3
+    assert ident(0xC0000000, 0xD0000000, 0xE0000000, ws=0xD0000000 + 4096) == -3
+    # spa_topk: idx_out over the scores
+    assert lib.spa_topk(2, 100, _fake(P), 10, _fake(P + 256), None) == -3

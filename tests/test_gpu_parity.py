@@ -12,6 +12,9 @@ import pytest
 import oracle
 import synth
 from helpers import check_near_ties, dev, has_gpu, host, rel_l2, tol_for
+from parity_cases import (ATTEND_CASES, ATTEND_MANY_CASES, BATCHED_EXACT_RHO, BATCHED_ID_RANKS, DREAM_STACK_K,
+                          FUSED_TOPK_SHAPES, LLADA_EXACT_K, LLADA_ID_RANKS, ROPE_STEP_CASES, SMALL_BF16, SMALL_STEP_K,
+                          fused_topk_ks)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs an MI355X")]
 
@@ -56,11 +59,13 @@ def _slice(cache, sel):
     return oracle.LayerCache(cache.k[sel], cache.v[sel], cache.h[sel], cache.p[sel])
 
 
-def _check_step(case, k, policy=oracle.POLICY_ALL, seqs=None):
+def _check_step(case, k, policy=oracle.POLICY_ALL, seqs=None, exact=False):
     """One cached step on the GPU against the oracle. Scores, the proxy cache and the untouched rows
     are checked for every sequence; block outputs for the sequences in `seqs` (default: all). The
     oracle only ever sees host inputs: when the GPU's set differs from the oracle's by near-ties,
-    the GPU's phases 2-3 are re-run on the oracle's set (spa_sparse_update) and compared with that."""
+    the GPU's phases 2-3 are re-run on the oracle's set (spa_sparse_update) and compared with that.
+    exact=True: the inputs leave no near-tie at the k-th boundary, so the GPU's set must equal the
+    oracle's in every sequence and the step's own block outputs are the ones compared."""
     import torch
     spa = _lib()
     s = case.shape
@@ -80,6 +85,8 @@ def _check_step(case, k, policy=oracle.POLICY_ALL, seqs=None):
     i_g = host(idx).astype(np.int64)
     same = True
     for b in range(s.batch):
+        if exact and k:
+            assert np.array_equal(i_g[b], idx_o[b]), f"sequence {b}: the update set differs from the oracle's"
         if k and check_near_ties(i_g[b], idx_o[b], s_o[b], k):
             same = same and b not in sel
     hk, hv, hh, hp = host(c.k), host(c.v), host(c.h), host(c.p)
@@ -109,14 +116,8 @@ def _check_step(case, k, policy=oracle.POLICY_ALL, seqs=None):
     return i_g, s_g
 
 
-SMALL_BF16 = [
-    synth.LayerShape(2, 200, 256, 4, 4, 64, 688, 32, "bf16"),      # ragged N, K tail in W_down (688)
-    synth.LayerShape(1, 333, 512, 8, 2, 128, 1024, 64, "bf16"),    # GQA, hd 128, ragged N
-]
-
-
 @pytest.mark.parametrize("shape_i", [0, 1])
-@pytest.mark.parametrize("k", [1, 37, 150])
+@pytest.mark.parametrize("k", SMALL_STEP_K)
 def test_layer_step_small_bf16(shape_i, k):
     shape = SMALL_BF16[shape_i]
     case = Case(shape, seed=10 + shape_i, n_drift=min(60, shape.n_tokens // 3))
@@ -213,11 +214,7 @@ def test_topk_bit_exact(b, n):
             assert got[bi].tolist() == oracle.select_topk(s[bi], k).tolist(), (bi, k)
 
 
-@pytest.mark.parametrize("shape", [SMALL_BF16[0], SMALL_BF16[1],
-                                   synth.LayerShape(5, 3, 128, 2, 2, 64, 256, 16, "bf16"),
-                                   synth.LayerShape(3, 1030, 256, 4, 4, 64, 688, 32, "bf16"),
-                                   synth.LayerShape(2, 3000, 256, 4, 4, 64, 688, 32, "bf16"),
-                                   synth.LayerShape(1, 4100, 256, 4, 4, 64, 688, 32, "bf16")])
+@pytest.mark.parametrize("shape", FUSED_TOPK_SHAPES)
 def test_layer_step_fused_topk_equals_spa_topk(shape):
     """The Top-k taken inside the cosine kernel of spa_layer_step (by the workgroup that completes each
     sequence) equals spa_topk on the scores that step returns, and the oracle's selection on them:
@@ -229,7 +226,7 @@ def test_layer_step_fused_topk_equals_spa_topk(shape):
     case = Case(s, seed=80 + s.n_tokens, n_drift=max(1, s.n_tokens // 5), warm="kv")
     w, c = case.device()
     x1 = dev(case.x1, s.dtype)
-    for k in sorted({1, s.n_tokens // 3, s.n_tokens - 1, s.n_tokens} - {0}):
+    for k in fused_topk_ks(s.n_tokens):
         idx = torch.full((s.batch, k), -1, dtype=torch.int32, device="cuda")
         scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
         spa.spa_layer_step(s, w, c, x1, k, 0, idx, scores, spa.alloc_workspace(s, k))
@@ -273,11 +270,7 @@ def _rope_bias_case(shape, seed, n_drift, bias=True):
     return case
 
 
-@pytest.mark.parametrize("shape,k", [
-    (synth.LayerShape(1, 333, 512, 8, 2, 128, 1024, 64, "bf16", rope_theta=1e6), 100),
-    (synth.LayerShape(2, 200, 256, 4, 4, 64, 688, 32, "bf16", rope_theta=1e4), 37),
-    (synth.LayerShape(1, 64, 256, 4, 4, 64, 688, 16, "f32", rope_theta=1e4), 16),
-])
+@pytest.mark.parametrize("shape,k", ROPE_STEP_CASES)
 def test_layer_step_rope_and_biases(shape, k):
     """Cached steps of layers with q/k/v biases and the rotary embedding (GQA, ragged N, fp32)."""
     _check_step(_rope_bias_case(shape, 70, shape.n_tokens // 5), k)
@@ -351,9 +344,7 @@ def test_layer_step_full_rank_identifier():
     s = synth.LayerShape(1, 256, 2048, 16, 16, 128, 1024, 2048, "bf16")
     _check_step(Case(s, seed=62, n_drift=40, warm="kv"), 64)
 
-@pytest.mark.parametrize("dtype,hd,hq,hkv,n,m", [("bf16", 128, 4, 4, 1024, 256), ("bf16", 64, 6, 2, 77, 13),
-                                                 ("f32", 64, 4, 4, 64, 16), ("f32", 128, 2, 1, 100, 70),
-                                                 ("bf16", 128, 28, 4, 300, 65)])
+@pytest.mark.parametrize("dtype,hd,hq,hkv,n,m", ATTEND_CASES)
 def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
     import torch
     spa = _lib()
@@ -372,8 +363,7 @@ def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
         assert rel_l2(got[bi], ref) <= tol_for(dtype), rel_l2(got[bi], ref)
 
 
-@pytest.mark.parametrize("b,hd,hq,hkv,n,m", [(8, 128, 32, 32, 333, 450), (8, 128, 32, 4, 1024, 256),
-                                             (4, 64, 64, 16, 100, 700)])
+@pytest.mark.parametrize("b,hd,hq,hkv,n,m", ATTEND_MANY_CASES)
 def test_attend_many_queries_matches_oracle(b, hd, hq, hkv, n, m):
     """Enough queries per head for the 256-query bf16 kernel (B H_q ceil(m / 256) >= 256 workgroups,
     query blocks at least 3/4 full): ragged key tiles (333, 100 keys), ragged last query blocks (450,
@@ -472,69 +462,158 @@ def test_sparse_update_unsorted_and_out_of_range_indices():
 
 
 # ---------------------------------------------------------------------------------------------
-# full-size layers: the llada-layer workload (N=1024, d=4096, r=128, k=256) and a Dream layer
+# full-size layers: the llada-layer workload (N=1024, d=4096, r=128, k=256), Dream layers at the
+# stack's row counts, and the batched stress layer (B=8, N=4096)
 # ---------------------------------------------------------------------------------------------
+def _redrift(case, n_drift, seed):
+    """A copy of `case` whose step input drifts on exactly n_drift rows per sequence (N(0, 0.5^2)
+    added; N(0, (1e-3)^2) on every other row). With k = n_drift the update set is the drifted rows,
+    whose cosines lie far below the others', so the step's own index sets and outputs are compared
+    with the oracle's (no near-tie fallback)."""
+    c = Case.__new__(Case)
+    c.shape, c.w, c.w_r, c.x0, c.cache0 = case.shape, case.w, case.w_r, case.x0, case.cache0
+    rng = np.random.default_rng([78, seed, n_drift])
+    c.x1, c.drifted = synth.drift_step(case.x0, n_drift, rng, case.shape.dtype)
+    return c
+
+
+def _kv_cache_case(s, w, x0, w_r):
+    """Host case whose cache holds the K/V of every token of x0, H^c = x0 and P^c = proxy(x0)."""
+    case = Case.__new__(Case)
+    case.shape, case.w, case.w_r, case.x0 = s, w, w_r, x0
+    kc, vc = oracle.kv_project(x0, w, s.head_dim, EPS, s.dtype)
+    pc = oracle.proxy(x0, w_r).astype(np.float32).astype(np.float64)
+    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(x0, np.float64), pc)
+    return case
+
+
 @pytest.fixture(scope="module")
 def llada_case():
+    """The llada-layer workload; one SVD of W_v gives the proxies of every rank the stack offers (the
+    rank-r proxy is the first r rows of the rank-512 one)."""
     wl = synth.WORKLOADS["llada-layer"]
     s = wl.shape
-    case = Case.__new__(Case)
-    case.shape = s
-    case.w = synth.layer_weights(wl)
-    case.w_r = synth.to_storage(oracle.singular_proxy(case.w["w_v"], case.w["g_attn"], s.rank), s.dtype)
+    w = synth.layer_weights(wl)
+    w512 = oracle.singular_proxy(w["w_v"], w["g_attn"], 512)
+    w_rs = {r: synth.to_storage(w512[:r], s.dtype) for r in sorted(set(LLADA_ID_RANKS) | {s.rank})}
     xs, drifted = synth.drift_sequence(wl, n_steps=1)
-    case.x0, case.x1, case.drifted = xs[0], xs[1], drifted[0]
-    kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
-    pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
-    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
+    case = _kv_cache_case(s, w, xs[0], w_rs[s.rank])
+    case.w_rs = w_rs
+    case.x1, case.drifted = xs[1], drifted[0]
     return case
+
+
+def _identify_check(case, s, w_r):
+    """spa_identify of case.x1 against the cached proxies of case.x0 under W_r (rank s.rank): P and the
+    scores against the oracle."""
+    import torch
+    spa = _lib()
+    pc = oracle.proxy(case.x0, w_r).astype(np.float32).astype(np.float64)
+    p_out = torch.empty(s.batch, s.n_tokens, s.rank, dtype=torch.float32, device="cuda")
+    scores = torch.empty(s.batch, s.n_tokens, dtype=torch.float32, device="cuda")
+    spa.spa_identify(s, dev(case.x1, s.dtype), spa.spa_pack_weight(dev(w_r, s.dtype)),
+                     torch.from_numpy(pc.astype(np.float32)).cuda(), p_out, scores, spa.alloc_workspace(s, 0))
+    torch.cuda.synchronize()
+    p_o, s_o = oracle.identify(case.x1, w_r, pc)
+    assert np.max(np.abs(host(scores) - s_o)) <= 1e-3
+    assert rel_l2(host(p_out), p_o) <= 1e-5
 
 
 @pytest.mark.timeout(600)
 def test_llada_layer_step_full_size(llada_case):
+    """The workload's own first step (f ~ U(0.1, 0.4): 165 drifted rows) at k = 256: the k-th
+    boundary falls among the undrifted rows, so near-ties are allowed there."""
     _check_step(llada_case, 256)
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("k", [51, 87, 130, 200])
-def test_llada_layer_step_full_size_ragged_rows(llada_case, k):
-    """Update sets whose row count is not a multiple of the GEMM tiles: at k = 130 and 200 gate/up and
-    W_down run on the LDS-DMA kernel with a last row tile of 2 or 72 valid rows; k = 51 and 87 (the
-    stack's first layers) take the 64-row register-path tiles and split-K W_o."""
-    _check_step(llada_case, k)
+@pytest.mark.parametrize("k", LLADA_EXACT_K)
+def test_llada_layer_step_full_size_exact_sets(llada_case, k):
+    """Exactly k drifted rows at the LLaDA stack's row counts (51 and 87 of its first layers, 123, and
+    k = 130, 200 whose last 128-row GEMM tile holds 2 and 72 rows) and at the workload's k = 256: the
+    step's own sets equal the oracle's and its own block outputs are compared."""
+    _check_step(_redrift(llada_case, k, 2), k, exact=True)
+
+
+def _full_value_proxy(case):
+    """The full-dimension Value identifier: W_r = W_v diag(g_attn), rounded to storage."""
+    return synth.to_storage(np.asarray(case.w["w_v"], np.float64) * np.asarray(case.w["g_attn"], np.float64)[None, :],
+                            case.shape.dtype)
+
+
+@pytest.mark.timeout(600)
+def test_llada_identify_full_value_rank(llada_case):
+    """The full-dimension Value identifier at the llada shape: r = d_kv = 4096 (spa_identify: P of
+    1024 x 4096 and the scores)."""
+    c = llada_case
+    _identify_check(c, c.shape.replace(rank=c.shape.d_kv), _full_value_proxy(c))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("r", LLADA_ID_RANKS)
+def test_llada_identify_ranks(llada_case, r):
+    """Identification at the llada shape for the other proxy ranks the stack offers."""
+    _identify_check(llada_case, llada_case.shape.replace(rank=r), llada_case.w_rs[r])
+
+
+@pytest.mark.timeout(600)
+def test_llada_layer_full_recompute_full_size(llada_case):
+    """The vanilla full recompute of the llada layer (M = 1024 rows in every product, 1024 queries per
+    head in attention) against the oracle's warm-up."""
+    import torch
+    spa = _lib()
+    c = llada_case
+    s = c.shape
+    dw = spa.upload_weights(c.w, c.w_r, s.dtype)
+    dc = spa.alloc_cache(s)
+    spa.spa_layer_full(s, dw, dc, dev(c.x1, s.dtype), spa.alloc_workspace(s, s.n_tokens))
+    torch.cuda.synchronize()
+    ref = oracle.warmup(c.x1, c.w, c.w_r, s.head_dim, EPS, s.dtype)
+    errs = {"K": rel_l2(host(dc.k), ref.k), "V": rel_l2(host(dc.v), ref.v), "H": rel_l2(host(dc.h), ref.h)}
+    assert max(errs.values()) <= 2e-2, errs
+    assert rel_l2(host(dc.p), ref.p) <= 1e-5
 
 
 @pytest.fixture(scope="module")
 def dream_case():
     wl = synth.WORKLOADS["dream-stack"]
     s = wl.shape
-    case = Case.__new__(Case)
-    case.shape = s
-    case.w = synth.layer_weights(wl, layer=9)
-    case.w_r = synth.to_storage(oracle.singular_proxy(case.w["w_v"], case.w["g_attn"], s.rank), s.dtype)
-    case.x0 = synth.first_hidden(wl, layer=9)
-    rng = np.random.default_rng([4, 9, 3])
-    case.x1, case.drifted = synth.drift_step(case.x0, 600, rng, s.dtype)
-    kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
-    pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
-    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
+    w = synth.layer_weights(wl, layer=9)
+    w_r = synth.to_storage(oracle.singular_proxy(w["w_v"], w["g_attn"], s.rank), s.dtype)
+    case = _kv_cache_case(s, w, synth.first_hidden(wl, layer=9), w_r)
+    case.x1, case.drifted = synth.drift_step(case.x0, 600, np.random.default_rng([4, 9, 3]), s.dtype)
     return case
 
 
 @pytest.mark.timeout(600)
 def test_dream_layer_step_full_size(dream_case):
+    """The peak layer of the Dream stack (layer 10, k = 512) with 600 drifted rows: near-ties allowed
+    at the boundary among the drifted rows."""
     _, ks = oracle.budget(28, 10, 0.25, 0.05, 0.08, dream_case.shape.n_tokens)
-    _check_step(dream_case, int(ks[9]))          # layer 10 = the peak: k = 512
+    assert int(ks[9]) == 512
+    _check_step(dream_case, 512)
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("k", [102, 311, 428])
+@pytest.mark.parametrize("k", DREAM_STACK_K)
 def test_dream_layer_step_full_size_stack_rows(dream_case, k):
-    """Row counts of other Dream stack layers (first layer k = 102; k = 311 and 428 on the way to the
-    peak): at 102 and 311 the GEMMs take the 64-row register-path tiles with two to four workgroups per
-    CU; at 428 (as at the peak, 512) gate/up runs one round of 256 x 256 tiles over its first 32768
-    columns and the remaining 5120 on a smaller tile."""
-    _check_step(dream_case, k)
+    """Exactly k drifted rows at row counts of the Dream stack's layers (k_1 = 102 up to the peak
+    k_10 = 512): the register-path tiles with two to four workgroups per CU, split-K W_down, and
+    the gate/up product split into whole rounds of 256 x 256 tiles plus a remainder of columns on a
+    smaller tile."""
+    _check_step(_redrift(dream_case, k, 4), k, exact=True)
+
+
+@pytest.mark.timeout(600)
+def test_dream_layer_step_full_value_identifier(dream_case):
+    """A Dream step whose identifier is the full Value projection (r = d_kv = 512, past one wave's
+    256-column pass in the cosine kernel), exactly k = 102 drifted rows."""
+    c = _redrift(dream_case, 102, 6)
+    c.w_r = _full_value_proxy(c)
+    c.shape = c.shape.replace(rank=c.shape.d_kv)
+    c.cache0 = oracle.LayerCache(c.cache0.k, c.cache0.v, c.cache0.h,
+                                 oracle.proxy(c.x0, c.w_r).astype(np.float32).astype(np.float64))
+    _check_step(c, 102, exact=True)
 
 
 @pytest.mark.timeout(900)
@@ -558,27 +637,67 @@ def test_dream_layer_full_recompute_full_size():
     assert max(errs.values()) <= 2e-2, errs
     assert rel_l2(host(c.p), ref.p) <= 1e-5
 
-@pytest.mark.timeout(900)
-def test_batched_stress_full_size_sampled():
-    """The batched stress layer at full size (B=8, N=4096, d=4096, r=128, rho=0.25 -> k=1024): every
-    sequence's scores, proxy cache, index set (near-ties) and untouched rows; the block outputs of the
-    first and the last sequence against the oracle."""
+
+@pytest.fixture(scope="module")
+def batched_case():
+    """The batched stress layer (B=8, N=4096, d=4096): one SVD of W_v gives the proxies of every swept
+    rank (the rank-r proxy is the first r rows of the rank-512 one)."""
     wl = synth.WORKLOADS["batched-stress"]
     s = wl.shape
+    w = synth.layer_weights(wl)
+    w512 = oracle.singular_proxy(w["w_v"], w["g_attn"], 512)
+    w_rs = {r: synth.to_storage(w512[:r], s.dtype) for r in (64, 128, 512)}
+    xs, drifted = synth.drift_sequence(wl, n_steps=1)
+    case = _kv_cache_case(s, w, xs[0], w_rs[s.rank])
+    case.w_rs = w_rs
+    case.x1, case.drifted = xs[1], drifted[0]
+    return case
+
+
+@pytest.mark.timeout(900)
+def test_batched_stress_full_size_sampled(batched_case):
+    """The workload's own step (614 drifted rows per sequence) at rho = 0.25 -> k = 1024: every
+    sequence's scores, proxy cache, index set (near-ties) and untouched rows; the block outputs of
+    the first and the last sequence against the oracle."""
+    wl = synth.WORKLOADS["batched-stress"]
+    s = batched_case.shape
     k = int(oracle.budget(1, 1, wl.rho, wl.rho, wl.rho, s.n_tokens)[1][0])
     assert k == 1024
-    case = Case.__new__(Case)
-    case.shape = s
-    case.w = synth.layer_weights(wl)
-    case.w_r = synth.to_storage(oracle.singular_proxy(case.w["w_v"], case.w["g_attn"], s.rank), s.dtype)
-    xs, drifted = synth.drift_sequence(wl, n_steps=1)
-    case.x0, case.x1, case.drifted = xs[0], xs[1], drifted[0]
-    kc, vc = oracle.kv_project(case.x0, case.w, s.head_dim, EPS, s.dtype)
-    pc = oracle.proxy(case.x0, case.w_r).astype(np.float32).astype(np.float64)
-    case.cache0 = oracle.LayerCache(kc, vc, np.asarray(case.x0, np.float64), pc)
-    i_g, _ = _check_step(case, k, seqs=[0, s.batch - 1])
+    i_g, _ = _check_step(batched_case, k, seqs=[0, s.batch - 1])
     for b in range(s.batch):   # the 614 drifted tokens of every sequence are all selected
-        assert set(case.drifted[b].tolist()) <= set(i_g[b].tolist())
+        assert set(batched_case.drifted[b].tolist()) <= set(i_g[b].tolist())
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rho", BATCHED_EXACT_RHO)
+def test_batched_stress_full_size_exact_sets(batched_case, rho):
+    """The sweep's rho = 0.08 and 0.16 points (k = 327, 655; M = 2616 and 5240 rows in the GEMMs) with
+    exactly k drifted rows per sequence: every sequence's set equals the oracle's; block outputs of the
+    first and the last sequence."""
+    s = batched_case.shape
+    k = int(oracle.budget(1, 1, rho, rho, rho, s.n_tokens)[1][0])
+    assert k == {0.08: 327, 0.16: 655}[rho]
+    _check_step(_redrift(batched_case, k, 5), k, seqs=[0, s.batch - 1], exact=True)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("r", BATCHED_ID_RANKS)
+def test_batched_identify_ranks(batched_case, r):
+    """Identification of the batched layer (B N = 32768 rows) at the sweep's other proxy ranks:
+    spa_identify's P and scores against the oracle."""
+    _identify_check(batched_case, batched_case.shape.replace(rank=r), batched_case.w_rs[r])
+
+
+def test_budget_through_the_c_abi():
+    """rho(l) and k_l of spa_budget equal the oracle's for the workloads' budgets (host entry point;
+    the CPU suite runs the same comparison on more parameters)."""
+    spa = _lib()
+    for args in [(32, 12, 0.25, 0.05, 0.08, 1024), (28, 10, 0.25, 0.05, 0.08, 2048), (1, 1, 0.25, 0.25, 0.25, 1024),
+                 (1, 1, 0.08, 0.08, 0.08, 4096), (1, 1, 0.16, 0.16, 0.16, 4096), (1, 1, 1.0, 1.0, 1.0, 4096)]:
+        rho, k = spa.spa_budget(*args)
+        rho_o, k_o = oracle.budget(*args)
+        assert k == k_o.tolist(), args
+        assert np.max(np.abs(np.array(rho) - rho_o)) <= 1e-15, args
 
 
 def _pack_reference(w, kind, e):
