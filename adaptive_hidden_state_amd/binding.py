@@ -20,8 +20,8 @@ SPA_PROXY_WRITE_ALL, SPA_PROXY_WRITE_SELECTED = 0, 1
 
 # Every symbol include/spacache.h declares.
 EXPORTS = ("spa_budget", "spa_packed_weight_bytes", "spa_pack_weight", "spa_workspace_bytes", "spa_layer_full",
-           "spa_layer_step", "spa_layer_step_timed", "spa_identify", "spa_topk", "spa_sparse_update", "spa_attend",
-           "spa_status_string")
+           "spa_layer_step", "spa_layer_step_timed", "spa_layer_step_noalloc", "spa_identify", "spa_topk",
+           "spa_sparse_update", "spa_attend", "spa_status_string")
 SPA_PACK_PLAIN, SPA_PACK_GATE_UP = 0, 1
 
 
@@ -74,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spa_layer_full": ([P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_layer_step": ([P, P, P, P, I32, I32, P, P, P, SZ, P], ctypes.c_int),
         "spa_layer_step_timed": ([P, P, P, P, I32, I32, P, P, P, SZ, P, P], ctypes.c_int),
+        "spa_layer_step_noalloc": ([P, P, P, P, I32, I32, P, P, P], ctypes.c_int),
         "spa_identify": ([P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "spa_topk": ([I32, I32, P, I32, P, P], ctypes.c_int),
         "spa_sparse_update": ([P, P, P, P, P, I32, P, SZ, P], ctypes.c_int),
@@ -241,6 +242,21 @@ def spa_layer_step(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, po
                                          int(k), int(policy), _ptr(idx_out, torch.int32, "idx_out"),
                                          _ptr(scores_out, torch.float32, "scores_out"), wp, wb, _stream(stream)),
            "spa_layer_step")
+
+
+def spa_layer_step_noalloc(shape, w: DeviceWeights, cache: DeviceCache, h_in, k: int, policy: int, idx_out,
+                           scores_out, stream=None):
+    """spa_layer_step on the library's static device scratch (no workspace argument, nothing allocated)."""
+    import torch
+    tdt = torch_dtype(shape.dtype)
+    s = make_shape(shape)
+    ws_ = _weights_struct(w, tdt, shape)
+    cs = _cache_struct(cache, tdt)
+    _check(load_library().spa_layer_step_noalloc(ctypes.byref(s), ctypes.byref(ws_), ctypes.byref(cs),
+                                                 _ptr(h_in, tdt, "h_in"), int(k), int(policy),
+                                                 _ptr(idx_out, torch.int32, "idx_out"),
+                                                 _ptr(scores_out, torch.float32, "scores_out"), _stream(stream)),
+           "spa_layer_step_noalloc")
 
 
 class HipEvents:

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "spacache.h"
 #include "step_plan.hpp"
 
@@ -76,7 +78,9 @@ struct Layout {
   size_t ppart, pbuf, scores, ssp, rinv, counters, q, o, y, z, ss32, gpart, total;
 };
 
-Layout make_layout(const Dims &D, int k_max) {
+// exact = true: the split-K partials are sized for the plans of exactly k_max rows per sequence (the
+// layout of one call); otherwise for any k <= k_max (a workspace shared by calls of different k).
+Layout make_layout(const Dims &D, int k_max, bool exact = false) {
   Layout L{};
   const size_t rows = (size_t)D.B * D.N;
   const size_t m = (size_t)D.B * (size_t)k_max;
@@ -101,7 +105,15 @@ Layout make_layout(const Dims &D, int k_max) {
   // Split-K partials of the four k-row GEMMs: gemm_partial_bound(M, N) covers every plan with
   // M <= B * k_max rows.
   size_t gp = 0;
-  if (m > 0) {
+  if (m > 0 && exact) {
+    const StepPlan P = plan_step(step_shape(D), k_max, false);
+    const GemmPlan *plans[4] = {&P.qkv, &P.wo, &P.gu, &P.dn};
+    const int widths[4] = {D.dq + 2 * D.dkv, D.d, 2 * D.Fp, D.d};
+    for (int i = 0; i < 4; ++i) {
+      const size_t b = plans[i]->splits > 1 ? gemm_partial_bytes(*plans[i], (int)m, widths[i]) : 0;
+      if (b > gp) gp = b;
+    }
+  } else if (m > 0) {
     const int widths[4] = {D.dq + 2 * D.dkv, D.d, 2 * D.Fp, D.d};
     for (int n : widths) {
       const size_t b = gemm_partial_bound((int)m, n);
@@ -351,6 +363,31 @@ int run_sparse(const Dims &D, const Layout &L, const StepPlan &P, const spa_laye
   return SPA_OK;
 }
 
+// Device scratch of spa_layer_step_noalloc, for callers that cannot allocate: one static array per
+// device, held until the process ends. Host code never uses the array's name as an address: each
+// device's address is looked up once (hipGetSymbolAddress with that device current) and kept.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the scratch array on the current device.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SPA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SPA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,9 +487,15 @@ int spa_layer_full(const spa_shape *shape, const spa_layer_weights *w, const spa
   return run_sparse(D, L, P, w, cache, h_in, nullptr, D.N, ws, stream, mk);
 }
 
-int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
-                         const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
-                         size_t ws_bytes, hipStream_t stream, spa_timing *timing) {
+}  // extern "C"
+
+namespace {
+
+// The cached step. noalloc: ws is ignored and the static scratch serves as the workspace, laid out
+// exactly for this call (SPA_ERR_WORKSPACE past kStaticScratchBytes).
+int layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache, const void *h_in,
+               int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws, size_t ws_bytes,
+               hipStream_t stream, spa_timing *timing, bool noalloc) {
   if (timing != nullptr) {
     if (timing->capacity < 0 || (timing->capacity > 0 && timing->marks == nullptr)) return SPA_ERR_INVALID_ARG;
     timing->count = 0;
@@ -466,7 +509,12 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
   if (policy != SPA_PROXY_WRITE_ALL && policy != SPA_PROXY_WRITE_SELECTED) return SPA_ERR_INVALID_ARG;
   if (k > 0 && idx_out == nullptr) return SPA_ERR_INVALID_ARG;
   if ((idx_out && !aligned16(idx_out)) || (scores_out && !aligned16(scores_out))) return SPA_ERR_ALIGN;
-  const Layout L = make_layout(D, k);
+  const Layout L = make_layout(D, k, noalloc);
+  if (noalloc) {
+    if (L.total > kStaticScratchBytes) return SPA_ERR_WORKSPACE;
+    if ((st = scratch_address(&ws)) != SPA_OK) return st;
+    ws_bytes = kStaticScratchBytes;
+  }
   if ((st = check_ws(ws, ws_bytes, L.total)) != SPA_OK) return st;
   {
     Span wr[7], rd[7];
@@ -491,6 +539,22 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
     SPA_TRY(mk.mark("proxy_copy_selected"));
   }
   return run_sparse(D, L, P, w, cache, h_in, idx_out, k, ws, stream, mk);
+}
+
+}  // namespace
+
+extern "C" {
+
+int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                         const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out, void *ws,
+                         size_t ws_bytes, hipStream_t stream, spa_timing *timing) {
+  return layer_step(shape, w, cache, h_in, k, policy, idx_out, scores_out, ws, ws_bytes, stream, timing, false);
+}
+
+int spa_layer_step_noalloc(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                           const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
+                           hipStream_t stream) {
+  return layer_step(shape, w, cache, h_in, k, policy, idx_out, scores_out, nullptr, 0, stream, nullptr, true);
 }
 
 int spa_layer_step(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,

@@ -182,6 +182,19 @@ int spa_layer_step_timed(const spa_shape *shape, const spa_layer_weights *w, con
                          const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
                          void *ws, size_t ws_bytes, hipStream_t stream, spa_timing *timing);
 
+/* spa_layer_step without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The library's own
+ * scratch serves as the workspace: a static device array of 64 MiB on each GPU, held until the
+ * process ends, laid out exactly for the call; the call allocates and frees nothing. Arguments,
+ * results and errors are those of spa_layer_step; SPA_ERR_WORKSPACE when the call would need more than
+ * 64 MiB of scratch (the llada-shaped layer of N = 1024, d = 4096, F = 12288 needs about 33 MiB at
+ * k = 256). The stream must belong to the current device. Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller. */
+int spa_layer_step_noalloc(const spa_shape *shape, const spa_layer_weights *w, const spa_layer_cache *cache,
+                           const void *h_in, int32_t k, int32_t policy, int32_t *idx_out, float *scores_out,
+                           hipStream_t stream);
+
 /* Phase 1 scores only ([PN] 整体框架 Phase 1; [GS] part 1), with w_r fragment-packed (spa_pack_weight of
  * the r x d matrix): p_out = X W_r^T (B x N x r float32) and,
  * when p_cache is not NULL, scores_out = cosine(p, p^c) (B x N). Never writes p_cache.

@@ -263,3 +263,20 @@ def test_alias_checks_of_every_written_buffer(lib):
     assert ident(0xC0000000, 0xD0000000, 0xE0000000, ws=0xD0000000 + 4096) == -3
     # spa_topk: idx_out over the scores
     assert lib.spa_topk(2, 100, _fake(P), 10, _fake(P + 256), None) == -3
+
+
+def test_noalloc_step_validation(lib):
+    """spa_layer_step_noalloc validates like spa_layer_step, and refuses a call whose exact layout
+    exceeds its 64 MiB of static scratch before touching the device."""
+    s = _shape()
+    w, c = _weights(), _cache()
+    call = lambda s, w, c, x, k=256, idx=0x90000000: lib.spa_layer_step_noalloc(
+        ctypes.byref(s), ctypes.byref(w) if w is not None else None, ctypes.byref(c), _fake(x) if x else None, k, 0,
+        _fake(idx) if idx else None, None, None)
+    assert call(s, None, c, X) == -1
+    assert call(s, _weights(misalign=1), c, X) == -4
+    assert call(s, w, _cache(h=X + 4096), X) == -3
+    assert call(s, w, c, X, k=2000) == -1
+    assert call(s, w, c, X, idx=0) == -1
+    big = _shape(batch=8, n_tokens=4096)
+    assert call(big, w, _cache(), X, k=1024, idx=0xF0000000) == -5
