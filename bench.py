@@ -175,16 +175,17 @@ def kernel_work(name, s, k):
     return gemm_work(name, s, M)
 
 
-def cpu_baseline(wl, w, w_r, xs, k, seconds):
-    """The oracle's cached layer step timed on the host cores (bounded sample)."""
+def cpu_baseline(wl, w, w_r, xs, k, seconds, threads=None):
+    """The oracle's cached layer step timed on the host cores (bounded sample); threads: limit the BLAS
+    thread pool to that many threads (None: the pool as configured)."""
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads, user_api="blas"):
+            return cpu_baseline(wl, w, w_r, xs, k, seconds)
     import numpy as np
     import oracle
     s = wl.shape
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     kc, vc = oracle.kv_project(xs[0], w, s.head_dim, s.norm_eps, s.dtype)
     pc = oracle.proxy(xs[0], w_r).astype(np.float32).astype(np.float64)
     cache = oracle.LayerCache(kc, vc, np.asarray(xs[0], np.float64), pc)
@@ -269,6 +270,36 @@ def base_line(args, wl, s, value, unit, ms_step, steps, warmup, data):
     }
 
 
+def timed_blocks(step, first, steps, blocks):
+    """Time exactly `steps` consecutive calls step(first), step(first + 1), ... as `blocks` consecutive
+    blocks of (nearly) equal size, with an event on the current stream between blocks and a
+    synchronize before the first and after the last. Returns the median over the blocks of the time
+    per step (ms) and the per-block values."""
+    import numpy as np
+    import torch
+    nb = max(1, min(blocks, steps))
+    sizes = [steps // nb + (1 if b < steps % nb else 0) for b in range(nb)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda.synchronize()
+    i = first
+    evs[0].record()
+    for b, n in enumerate(sizes):
+        for _ in range(n):
+            step(i)
+            i += 1
+        evs[b + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[b].elapsed_time(evs[b + 1]) / sizes[b] for b in range(nb)]
+    return float(np.median(per)), per
+
+
+def block_stats(per, ms):
+    """Summary of a timed_blocks result for the bench line."""
+    return {"blocks": len(per), "ms_per_step_blocks": [round(v, 5) for v in per],
+            "ms_per_step_mean": round(sum(per) / len(per), 5),
+            "spread": round((max(per) - min(per)) / ms, 4) if ms > 0 else None}
+
+
 def timed_kernels(spa, calls, reps):
     """Per-kernel durations (us, median over reps) of a sequence of spa_layer_step_timed calls;
     `calls(ev)` runs one pass and returns [(name, ms), ...] summed over its layers."""
@@ -324,21 +355,6 @@ def run_layer(args, wl):
         spa.spa_layer_full(s, dws[r], caches[r], xds[r][0], ws)
     torch.cuda.synchronize()
 
-    # vanilla full recompute of the same layer (the "Baseline 100%" path), for the speedup
-    scratch = [spa.alloc_cache(s) for _ in range(R)]
-    for r in range(R):
-        spa.spa_layer_full(s, dws[r], scratch[r], xds[r][1], ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_full = 4 * R
-    e0.record()
-    for i in range(n_full):
-        spa.spa_layer_full(s, dws[i % R], scratch[i % R], xds[i % R][1 + (i // R) % n_in], ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_full = e0.elapsed_time(e1) / n_full
-    del scratch
-
     def which(i):  # step i -> (instance, input step)
         return i % R, 1 + (i // R) % n_in
 
@@ -346,27 +362,39 @@ def run_layer(args, wl):
         r, j = which(i)
         spa.spa_layer_step(s, dws[r], caches[r], xds[r][j], k, spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
 
-    # one captured HIP graph per (instance, input step); every launch of a step is stream-ordered and
-    # allocation-free, so the step is capturable as is
+    # the vanilla full recompute of the same layer (the "Baseline 100%" path, every token updated), into
+    # caches of its own, for the speedup; timed the same way as the cached step
+    scratch = [spa.alloc_cache(s) for _ in range(R)]
+
+    def eager_full(i):
+        r, j = which(i)
+        spa.spa_layer_full(s, dws[r], scratch[r], xds[r][j], ws)
+
+    # one captured HIP graph per (instance, input step) for each path; every launch of a step is
+    # stream-ordered and allocation-free, so the step is capturable as is
     graphs = capture(args, [lambda i=i: eager_step(i) for i in range(R * n_in)]) if args.graph else None
+    graphs_full = capture(args, [lambda i=i: eager_full(i) for i in range(R * n_in)]) if args.graph else None
 
-    def step(i):
-        if graphs is not None:
-            r, j = which(i)
-            graphs[r * n_in + (j - 1)].replay()
-        else:
-            eager_step(i)
+    def replay(gs, eager):
+        def run(i):
+            if gs is not None:
+                r, j = which(i)
+                gs[r * n_in + (j - 1)].replay()
+            else:
+                eager(i)
+        return run
 
+    step, full = replay(graphs, eager_step), replay(graphs_full, eager_full)
     for i in range(warmup):
         step(i)
+        full(i)
     torch.cuda.synchronize()
-    log(f"[bench] timing {steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances)")
-    e0.record()
-    for i in range(steps):
-        step(warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+    log(f"[bench] timing {steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances, "
+        f"{args.blocks} blocks)")
+    ms_step, per_step = timed_blocks(step, warmup, steps, args.blocks)
+    log(f"[bench] timing {steps} full recomputes")
+    ms_full, per_full = timed_blocks(full, warmup, steps, args.blocks)
+    del scratch, graphs_full
 
     # per-kernel durations: HIP events between the kernels of the same step sequence
     it = iter(range(10 ** 9))
@@ -392,13 +420,18 @@ def run_layer(args, wl):
     line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
     line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
     line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
-    line["timing"] = {"graphs": graphs is not None, "instances": R,
-                      "note": "per-kernel us from HIP events recorded between kernels on the launch stream"}
+    line["timing"] = {"graphs": graphs is not None, "instances": R, **block_stats(per_step, ms_step),
+                      "full_recompute": block_stats(per_full, ms_full),
+                      "note": "ms_per_step = median over the blocks of the timed steps; per-kernel us from HIP "
+                              "events recorded between kernels on the launch stream"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
     line["gpu"] = gpu_info()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(wl, w, np.asarray(w_r, np.float64), xs, k, args.cpu_seconds)
+        log("[bench] timing the CPU oracle on one core")
+        line["cpu_baseline_1core"] = cpu_baseline(wl, w, np.asarray(w_r, np.float64), xs, k, args.cpu_seconds,
+                                                  threads=1)
     else:
         line["cpu_baseline"] = None
     return line
@@ -518,14 +551,9 @@ def run_stack(args, wl):
     for t in range(warmup):
         step(t)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {steps} denoising steps x {L} layers ({'graph' if graphs else 'eager'})")
-    e0.record()
-    for t in range(steps):
-        step(warmup + t)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+    log(f"[bench] timing {steps} denoising steps x {L} layers ({'graph' if graphs else 'eager'}, "
+        f"{args.blocks} blocks)")
+    ms_step, per_step = timed_blocks(step, warmup, steps, args.blocks)
 
     def one(ev):
         feed(warmup + steps)
@@ -546,15 +574,42 @@ def run_stack(args, wl):
             b, f = b + bb, f + ff
         work[n] = (b, f)
 
-    # vanilla decoding: every layer fully recomputed at every step
-    n_full = max(2, min(steps, 8))
-    e0.record()
-    for t in range(n_full):
-        feed(warmup + steps + 1 + t)
-        chain(True)
-    e1.record()
+    # Parallel decoding: of the u positions a denoising step unmasks (fresh embedding rows at layer 0),
+    # how many each layer's update set recomputes (one untimed step per u, from the current caches)
+    coverage = {}
+    for uu in sorted({16, 64, 256, u}):
+        if uu > N:
+            continue
+        pos_u, _ = synth.unmask_schedule(wl, s, per_step=uu)
+        # fresh rows (a stream of their own), so every one of the uu positions changes
+        fresh = synth.normal_device((B, uu, s.d_model), wl.config_id, 100 + uu, synth.STREAM_DRIFT, dtype=s.dtype)
+        x_buf.index_copy_(1, pos_u[0], fresh)
+        unmasked = set(pos_u[0].tolist())
+        x, frac = x_buf, []
+        for l in range(L):
+            spa.spa_layer_step(s, layers[l], caches[l], x, ks[l], spa.SPA_PROXY_WRITE_ALL, idx, scores, ws)
+            sel = idx.view(-1)[:B * ks[l]].view(B, ks[l]).cpu().numpy()
+            frac.append(float(np.mean([len(unmasked & set(sel[b].tolist())) / uu for b in range(B)])))
+            x = caches[l].h
+        coverage[str(uu)] = {"per_layer": [round(f, 4) for f in frac], "mean": round(float(np.mean(frac)), 4),
+                             "min": round(min(frac), 4)}
     torch.cuda.synchronize()
-    ms_full = e0.elapsed_time(e1) / n_full
+
+    # vanilla decoding: every layer fully recomputed at every step (the same unmasking copy, graph-replayed
+    # like the cached step); it overwrites the caches, so it is timed last
+    graphs_full = capture(args, [lambda: chain(True)]) if args.graph else None
+
+    def full_step(t):
+        feed(t)
+        if graphs_full is not None:
+            graphs_full[0].replay()
+        else:
+            chain(True)
+
+    n_full = max(args.blocks, min(steps, 8))
+    full_step(warmup + steps + 1)
+    log(f"[bench] timing {n_full} full recomputes of the stack")
+    ms_full, per_full = timed_blocks(full_step, warmup + steps + 2, n_full, args.blocks)
 
     line = base_line(args, wl, s, u * B / (ms_step * 1e-3), "tokens/s", ms_step, steps, warmup,
                      "synthetic (seeded random-init layers with a planted Value spectrum, drawn on the device; "
@@ -571,33 +626,33 @@ def run_stack(args, wl):
     line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
     line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
     line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
-    line["timing"] = {"graphs": graphs is not None, "instances": 1,
-                      "note": "ms_per_step = one denoising step through all layers (the unmasking copy "
-                              "included); per-kernel us summed over the layers of one step"}
+    line["unmasked_rows_in_update_set"] = coverage
+    line["timing"] = {"graphs": graphs is not None, "instances": 1, **block_stats(per_step, ms_step),
+                      "full_recompute": block_stats(per_full, ms_full),
+                      "note": "ms_per_step = median over the blocks of one denoising step through all layers (the "
+                              "unmasking copy included); per-kernel us summed over the layers of one step"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
     line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline_sample(wl, s, pair, ks, [0, l_p - 1, L - 1], x0, pos, rows,
-                                                   args.cpu_seconds, args.identifier, bias)
+        log("[bench] timing the CPU oracle over the first denoising steps of every layer")
+        line["cpu_baseline"] = cpu_baseline_stack(wl, s, pair, ks, x0, pos, rows, args.cpu_steps, args.identifier,
+                                                  bias)
     return line
 
 
-def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, identifier, bias=False):
-    """The oracle's cached step on a sample of one stack's layers (each with its own k_l), from the
-    step-0 embeddings and the first unmasking step, within a bounded time."""
+def cpu_baseline_stack(wl, s, pair, ks, x0, pos, rows, n_steps, identifier, bias=False):
+    """The oracle over the first n_steps denoising steps of the whole stack, on its own chain: every
+    layer's warm-up from the step-0 embeddings (untimed), then each step unmasks its positions in the
+    layer-0 input and runs the cached step of every layer, layer l reading layer l-1's output (timed)."""
     import numpy as np
     import oracle
     import adaptive_hidden_state_amd as spa
     import synth
+    L = len(ks)
     threads = blas_threads()
-    x0h = x0.float().cpu().numpy().astype(np.float64)
-    x1 = x0.clone()
-    x1.index_copy_(1, pos[0], rows[0])
-    x1h = x1.float().cpu().numpy().astype(np.float64)
-    done, el = 0, 0.0
-    for l in sample_layers:
+    layers = []
+    for l in range(L):   # host copies of the layers' weights (the same seeded draws as the GPU's)
         w = synth.layer_weights_device(wl, l + 1, pair, shape=s, qkv_bias=bias)
         if identifier == "full":
             w_r = w["w_v"].float().cpu().numpy().astype(np.float64)
@@ -606,20 +661,35 @@ def cpu_baseline_sample(wl, s, pair, ks, sample_layers, x0, pos, rows, seconds, 
             w_r = synth.to_storage(w_r.cpu().numpy(), s.dtype).astype(np.float64)
         wh = host_weights(w)
         wh["rope_theta"] = s.rope_theta
+        layers.append((wh, w_r))
         del w
-        kc, vc = oracle.kv_project(x0h, wh, s.head_dim, s.norm_eps, s.dtype)
-        pc = oracle.proxy(x0h, w_r).astype(np.float32).astype(np.float64)
-        cache = oracle.LayerCache(kc, vc, x0h.copy(), pc)
+    emb = x0.float().cpu().numpy().astype(np.float64)
+    caches, x = [], emb
+    t0 = time.perf_counter()
+    for l in range(L):
+        wh, w_r = layers[l]
+        caches.append(oracle.warmup(x, wh, w_r, s.head_dim, s.norm_eps, s.dtype))
+        x = caches[l].h
+    warm_s = time.perf_counter() - t0
+    done, el = 0, 0.0
+    for t in range(n_steps):
+        emb = emb.copy()
+        emb[:, pos[t].cpu().numpy()] = rows[t].float().cpu().numpy()
+        x = emb
         t0 = time.perf_counter()
-        oracle.cached_layer_step(x1h, wh, w_r, cache, ks[l], s.head_dim, s.norm_eps, s.dtype)
+        for l in range(L):
+            wh, w_r = layers[l]
+            caches[l], _, _ = oracle.cached_layer_step(x, wh, w_r, caches[l], ks[l], s.head_dim, s.norm_eps,
+                                                       s.dtype)
+            x = caches[l].h
+            done += 1
         el += time.perf_counter() - t0
-        done += 1
-        if el >= seconds:
-            break
     return {"value": done / el, "unit": "layer-steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one cached step of layers {[l + 1 for l in sample_layers[:done]]} of {wl.name} "
-                      f"(k = {[ks[l] for l in sample_layers[:done]]}, B={s.batch}, N={s.n_tokens}, d={s.d_model}) "
-                      f"by the NumPy float64 oracle, {el:.1f} s"}
+            "sample": f"the first {n_steps} denoising steps of {wl.name} through all {L} layers (k_l = the "
+                      f"budget's, B={s.batch}, N={s.n_tokens}, d={s.d_model}) by the NumPy float64 oracle on its "
+                      f"own chain: {done} cached layer steps in {el:.1f} s (warm-up of every layer, untimed: "
+                      f"{warm_s:.1f} s)",
+            "tokens_per_s": round(len(pos[0]) * s.batch * n_steps / el, 4)}
 
 
 def blas_threads():
@@ -660,7 +730,6 @@ def run_batched(args, wl):
     del w
     xs = synth.drift_sequence_device(wl, s0)
     n_in = len(xs) - 1
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     sweep, head = [], None
     peak_flops = PEAK_BF16_TFLOPS
     for r in ranks:
@@ -680,24 +749,18 @@ def run_batched(args, wl):
             for i in range(warmup):
                 step(i)
             torch.cuda.synchronize()
-            e0.record()
-            for i in range(steps):
-                step(warmup + i)
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
+            ms, per = timed_blocks(step, warmup, steps, args.blocks)
             work = {n: kernel_work(n, s, k) for n in step_kernels(s)}
             floor = ideal_floor_us(work, peak_flops) / 1e3
             pt = {"rank": r, "rho": rho, "k": k, "ms_per_step": round(ms, 4),
                   "layer_steps_per_s": round(B / (ms * 1e-3), 2), "ideal_floor_ms": round(floor, 4),
-                  "floor_frac": round(floor / ms, 4)}
+                  "floor_frac": round(floor / ms, 4), "spread": block_stats(per, ms)["spread"]}
             if rho == 1.0:
-                e0.record()
-                for i in range(steps):
+                def full(i):
                     spa.spa_layer_full(s, dw, cache, xs[1 + i % n_in], ws)
-                e1.record()
-                torch.cuda.synchronize()
-                pt["full_recompute_ms"] = round(e0.elapsed_time(e1) / steps, 4)
+
+                ms_f, per_f = timed_blocks(full, 0, steps, args.blocks)
+                pt["full_recompute_ms"] = round(ms_f, 4)
             log(f"[bench] {pt}")
             sweep.append(pt)
             if r == s0.rank and rho == wl.rho:
@@ -725,8 +788,9 @@ def run_batched(args, wl):
     line["sweep"] = sweep
     line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
     line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
-    line["timing"] = {"graphs": False, "instances": 1,
-                      "note": "eager launches (steps of milliseconds); per-kernel us at the headline point"}
+    line["timing"] = {"graphs": False, "instances": 1, "blocks": args.blocks,
+                      "note": "eager launches (steps of milliseconds); every ms_per_step is the median over the "
+                              "blocks of its timed steps; per-kernel us at the headline point"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
     line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
@@ -774,10 +838,14 @@ def main():
     ap.add_argument("--workload", default="llada-layer",
                     choices=["llada-layer", "tiny-f32", "llada-stack", "dream-stack", "batched-stress"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-steps", type=int, default=2,
+                    help="stacks: denoising steps through every layer that the CPU oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--instances", type=int, default=4,
                     help="independent layer instances visited in turn (defeats Infinity-Cache reuse)")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="time eager launches")
+    ap.add_argument("--blocks", type=int, default=5,
+                    help="the timed steps run as this many consecutive blocks; ms_per_step is their median")
     ap.add_argument("--budget", choices=["adaptive", "uniform"], default="adaptive",
                     help="stacks: piecewise-Gaussian rho(l), or its mean on every layer")
     ap.add_argument("--rank", type=int, default=None, help="stacks: proxy rank r")
