@@ -396,62 +396,70 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
   }
 }
 
-// Many sparse queries per head (bf16): one workgroup = (sequence, query head, block of 256 queries),
-// four waves of 64 queries each (two 32-query MFMA column blocks). All four waves stream every key of
-// the head through a double-buffered stage that they load together (one barrier per 32-key tile), so
-// each K/V byte fetched from L2 serves 256 queries, and each K or V^T fragment read from LDS feeds
-// two MFMAs (one per query block): half the LDS bytes per MFMA of the 32-query waves. No key split,
-// hence no merge: the softmax state stays in the wave and the output is normalised in place.
-template <int HD> struct WideAttnCfg {
-  static constexpr int QPW = 64, W = 4, Q = QPW * W;               // queries per wave / per workgroup
+// Many query rows per KV head (bf16): the query heads of a KV group packed into the MFMA rows. One
+// workgroup = (sequence b, KV head g, block of 256 packed rows). The packed rows of (b, g) are its m
+// queries times its grp query heads, query-major: row t is query t / grp of query head g grp + t % grp,
+// so with grouped-query attention every K/V byte fetched from L2 serves all the heads that read it
+// (Dream: 7 per KV head). Eight waves of 32 rows (two per SIMD, so one wave's MFMAs overlap another's
+// softmax and LDS traffic) stream every 32-key tile of the head through a double-buffered LDS stage that
+// they load together (one barrier per tile). S^T = K Q^T and O^T = V^T P^T on 32x32 MFMA blocks, online
+// softmax in fp32 base 2 with a lazily moved reference maximum, as in attention_kernel; no key split,
+// so the output is normalised in place. (Measured on MI355X: 807 us against 935 for four waves of 64
+// rows at B = 8, N = 4096, 32 heads, 1024 queries; a key split over workgroups with a merge of the
+// partial states lost to attention_kernel at every row count too small to fill the chip without it.)
+template <int HD, int QB, int NW> struct PackAttnCfg {
+  static constexpr int W = NW, QPW = 32 * QB, R = QPW * W;         // waves, rows per wave / per workgroup
   static constexpr int KT = 32;                                    // keys per tile
   static constexpr int KROWB = HD * 2 + 16, VROWB = KT * 2 + 16;   // K row / V^T row strides (bytes)
   static constexpr int STAGE = KT * KROWB + HD * VROWB;
   static constexpr int OROWB = (HD + 4) * 4;                       // staged fp32 output row
-  static constexpr int OUT = W * QPW * OROWB;
+  static constexpr int OUT = W * 32 * OROWB;                       // one 32-row block per wave at a time
   static constexpr int LDS = 2 * STAGE > OUT ? 2 * STAGE : OUT;
-  static constexpr int KCH = KT * HD / 8 / (64 * W);               // K 16-byte chunks per lane per tile
+  static constexpr int KCHUNKS = KT * HD / 8;                      // K 16-byte chunks per tile
+  static constexpr int KCH = (KCHUNKS + 64 * W - 1) / (64 * W);    // per lane (the last pass partial)
   static constexpr int VTASKS = (KT / 8) * (HD / 8);               // 8x8 V blocks per tile
   static constexpr int VW = VTASKS / W;                            // per wave (one per lane < VW)
-  static_assert(KCH >= 1 && KT * HD / 8 % (64 * W) == 0 && VTASKS % W == 0 && VW <= 64, "tile split");
+  static_assert(QB == 1 || QB == 2, "one or two column blocks per wave");
+  static_assert((KCHUNKS % (64 * W) == 0 || KCH == 1) && VTASKS % W == 0 && VW <= 64, "tile split");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int HD>
-__global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__restrict__ q,
-                                                             const bf16_t *__restrict__ kc,
-                                                             const bf16_t *__restrict__ vc, bf16_t *__restrict__ o,
-                                                             int m_per_seq, int n_tok, int hq, int hkv, int qblocks,
-                                                             int nwg, float scale_log2) {
+template <int HD, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t *__restrict__ q,
+                                                                   const bf16_t *__restrict__ kc,
+                                                                   const bf16_t *__restrict__ vc,
+                                                                   bf16_t *__restrict__ o, int m_per_seq, int n_tok,
+                                                                   int hq, int hkv, int rblocks, int nwg,
+                                                                   float scale_log2) {
   typedef bf16_t T;
-  typedef WideAttnCfg<HD> C;
+  typedef PackAttnCfg<HD, QB, NW> C;
   constexpr int KT = C::KT, KROWB = C::KROWB, VROWB = C::VROWB, KCH = C::KCH, VW = C::VW;
   constexpr int QSTEPS = HD / 16, HB = HD / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
+  // XCD-aware order (hardware hands workgroup i to XCD i % 8): each XCD runs a contiguous range of
+  // (sequence, KV head, row block), so the row blocks that read one head's K/V share an L2
   const int nb = gridDim.x;
   const int lid = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (lid >= nwg) return;  // grid padding (whole workgroup, before any barrier)
   const int grp = hq / hkv;
-  const int qb = lid % qblocks;
-  int rest = lid / qblocks;
-  const int h_in = rest % grp;
-  rest /= grp;
-  const int g = rest % hkv;
-  const int b = rest / hkv;
-  const int h = g * grp + h_in;
+  const int rb = lid % rblocks;
+  const int g = (lid / rblocks) % hkv;
+  const int b = lid / rblocks / hkv;
+  const int rows = grp * m_per_seq;            // packed rows of (b, g)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int m0 = qb * C::Q + wave * C::QPW;  // this wave's queries m0 .. m0 + 63
-  const int ldq = hq * HD;
+  const int row0 = rb * C::R + wave * C::QPW;  // this wave's first packed row
   auto stage = [&](int buf) { return smem + buf * C::STAGE; };
+  // output row (in the B x m x hq layout of q and o) of packed row t of (b, g)
+  auto out_row = [&](int t) { return ((long long)b * m_per_seq + t / grp) * hq + g * grp + t % grp; };
 
-  // Q fragments of both query blocks: B operand of S^T = K Q^T (column = query lane % 32)
-  u32x4 qf[2][QSTEPS];
+  // Q fragments of the wave's column blocks: B operand of S^T = K Q^T (column = packed row lane % 32)
+  u32x4 qf[QB][QSTEPS];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int qrow = min(m0 + 32 * j + (lane & 31), m_per_seq - 1);
-    const T *qp = q + ((size_t)b * m_per_seq + qrow) * ldq + (size_t)h * HD;
+  for (int j = 0; j < QB; ++j) {
+    const int t = min(row0 + 32 * j + (lane & 31), rows - 1);
+    const T *qp = q + out_row(t) * HD;
 #pragma unroll
     for (int st = 0; st < QSTEPS; ++st) qf[j][st] = ld16(qp + st * 16 + (lane >> 5) * 8);
   }
@@ -460,14 +468,19 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
   const T *kbase = kc + head_off;
   const T *vbase = vc + head_off;
 
-  floatx16 oacc[2][HB];
+  floatx16 oacc[QB][HB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < QB; ++j)
 #pragma unroll
     for (int i = 0; i < HB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[j][i][r] = 0.f;
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float mrun[QB], lrun[QB];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    mrun[j] = -INFINITY;
+    lrun[j] = 0.f;
+  }
 
   // tile loads split over the four waves: K chunks c = lane + 64 (4 jj + wave); V block v = VW wave + lane
   u32x4 rk[KCH], rv[8];
@@ -481,13 +494,16 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
   const int vtask = wave * VW + (vlane ? lane : 0);
   const int vkb = vtask % (KT / 8), vcc = vtask / (KT / 8);
   const int voff = vkb * 8 * HD + vcc * 8;
+  // lanes past the tile's K chunks (hd 64 with eight waves) load and store none
+  auto kchunk = [&](int jj) { return C::KCHUNKS % (64 * C::W) == 0 || lane + 64 * (jj * C::W + wave) < C::KCHUNKS; };
   auto gload = [&](int t) {
     const int key0 = t * KT;
     if (key0 + KT <= n_tok) {
       const T *kt = kbase + (size_t)key0 * HD;
       const T *vt = vbase + (size_t)key0 * HD;
 #pragma unroll
-      for (int jj = 0; jj < KCH; ++jj) rk[jj] = ld16(kt + koff[jj]);
+      for (int jj = 0; jj < KCH; ++jj)
+        if (kchunk(jj)) rk[jj] = ld16(kt + koff[jj]);
       if (vlane) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) rv[e] = ld16(vt + voff + e * HD);
@@ -496,7 +512,7 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
 #pragma unroll
       for (int jj = 0; jj < KCH; ++jj) {
         const int key = min(key0 + koff[jj] / HD, n_tok - 1);
-        rk[jj] = ld16(kbase + (size_t)key * HD + koff[jj] % HD);
+        if (kchunk(jj)) rk[jj] = ld16(kbase + (size_t)key * HD + koff[jj] % HD);
       }
       if (vlane) {
 #pragma unroll
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
 #pragma unroll
     for (int jj = 0; jj < KCH; ++jj) {
       const int c = lane + 64 * (jj * C::W + wave);
-      st16(ks + (c / (HD / 8)) * KROWB + (c % (HD / 8)) * 16, rk[jj]);
+      if (kchunk(jj)) st16(ks + (c / (HD / 8)) * KROWB + (c % (HD / 8)) * 16, rk[jj]);
     }
     if (vlane) {
       u32x4 tr[8];
@@ -522,37 +538,37 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
     }
   };
 
-  // S^T = K Q^T of the tile in stage buf, both query blocks (each K fragment feeds two MFMAs)
-  auto qk = [&](int buf, floatx16 (&s)[2]) {
+  // S^T = K Q^T of the tile in stage buf, every column block (each K fragment feeds QB MFMAs)
+  auto qk = [&](int buf, floatx16 (&sc)[QB]) {
     const char *krow = stage(buf) + (lane & 31) * KROWB + (lane >> 5) * 16;
 #pragma unroll
-    for (int jq = 0; jq < 2; ++jq)
+    for (int jq = 0; jq < QB; ++jq)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[jq][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[jq][r] = 0.f;
 #pragma unroll
     for (int st = 0; st < QSTEPS; ++st) {
       const u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + st * 32);
-      s[0] = mfma32(kf, qf[0][st], s[0]);
-      s[1] = mfma32(kf, qf[1][st], s[1]);
+#pragma unroll
+      for (int jq = 0; jq < QB; ++jq) sc[jq] = mfma32(kf, qf[jq][st], sc[jq]);
     }
   };
   // Online softmax of tile t in place (scores -> probabilities). masked: the tile reaches past the
   // last key (a runtime branch: two inlined variants would not fit the register file).
-  auto softmax = [&](int t, floatx16 (&s)[2], bool masked) {
+  auto softmax = [&](int t, floatx16 (&sc)[QB], bool masked) {
 #pragma unroll
-    for (int jq = 0; jq < 2; ++jq) {
+    for (int jq = 0; jq < QB; ++jq) {
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * KT + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (key >= n_tok) s[jq][r] = -INFINITY;
+          if (key >= n_tok) sc[jq][r] = -INFINITY;
         }
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[jq][r]);
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[jq][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
-      // reference maximum that moves only when a query's maximum exceeds it by more than 8 (p <= 2^8)
+      // reference maximum that moves only when a row's maximum exceeds it by more than 8 (p <= 2^8)
       const float mnew = fmaxf(mrun[jq], tmax);
       const bool grow = mnew > mrun[jq] + 8.f;
       if (__any(grow)) {
@@ -567,26 +583,26 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[jq][r], scale_log2, -msub));
-        s[jq][r] = p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[jq][r], scale_log2, -msub));
+        sc[jq][r] = p;
         psum += p;
       }
       lrun[jq] += psum;
     }
   };
-  // O^T += V^T P^T from the tile in stage buf, each V^T fragment shared by the two query blocks
-  auto pv = [&](int buf, const floatx16 (&s)[2]) {
+  // O^T += V^T P^T from the tile in stage buf, each V^T fragment shared by the column blocks
+  auto pv = [&](int buf, const floatx16 (&sc)[QB]) {
     const char *vts = stage(buf) + KT * KROWB;
     const int G = lane >> 5;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      u32x4 pf[2];
+      u32x4 pf[QB];
 #pragma unroll
-      for (int jq = 0; jq < 2; ++jq) {
-        pf[jq][0] = pack_bf16x2(s[jq][half * 8 + 0], s[jq][half * 8 + 1]);
-        pf[jq][1] = pack_bf16x2(s[jq][half * 8 + 2], s[jq][half * 8 + 3]);
-        pf[jq][2] = pack_bf16x2(s[jq][half * 8 + 4], s[jq][half * 8 + 5]);
-        pf[jq][3] = pack_bf16x2(s[jq][half * 8 + 6], s[jq][half * 8 + 7]);
+      for (int jq = 0; jq < QB; ++jq) {
+        pf[jq][0] = pack_bf16x2(sc[jq][half * 8 + 0], sc[jq][half * 8 + 1]);
+        pf[jq][1] = pack_bf16x2(sc[jq][half * 8 + 2], sc[jq][half * 8 + 3]);
+        pf[jq][2] = pack_bf16x2(sc[jq][half * 8 + 4], sc[jq][half * 8 + 5]);
+        pf[jq][3] = pack_bf16x2(sc[jq][half * 8 + 6], sc[jq][half * 8 + 7]);
       }
       const int c0 = (half * 16 + 4 * G) * 2, c1 = c0 + 16;
 #pragma unroll
@@ -595,8 +611,8 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
         const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
         const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[0][hb] = mfma32(vf, pf[0], oacc[0][hb]);
-        oacc[1][hb] = mfma32(vf, pf[1], oacc[1][hb]);
+#pragma unroll
+        for (int jq = 0; jq < QB; ++jq) oacc[jq][hb] = mfma32(vf, pf[jq], oacc[jq][hb]);
       }
     }
   };
@@ -606,63 +622,63 @@ __global__ __launch_bounds__(256) void attention_wide_kernel(const bf16_t *__res
   lstore(0);
   gload(1);
   __syncthreads();
-  for (int i = 0; i < ntiles; ++i) {
-    floatx16 s[2];
-    qk(i & 1, s);
-    softmax(i, s, i * KT + KT > n_tok);
-    pv(i & 1, s);
-    if (i + 1 < ntiles) {
-      lstore((i + 1) & 1);
-      gload(i + 2);
+  for (int t = 0; t < ntiles; ++t) {
+    floatx16 sc[QB];
+    qk(t & 1, sc);
+    softmax(t, sc, t * KT + KT > n_tok);
+    pv(t & 1, sc);
+    if (t + 1 < ntiles) {
+      lstore((t + 1) & 1);
+      gload(t + 2);
     }
-    __syncthreads();  // tile i + 1 stored; tile i read by every wave (its buffer is refilled next)
+    __syncthreads();  // tile t + 1 stored; tile t read by every wave (its buffer is refilled next)
   }
 
-  // Normalise and stage this wave's 64 x HD outputs row-major in its own LDS region (the stages are
-  // free after the last barrier), then write whole 16-byte rows pieces.
-  char *ob = smem + wave * C::QPW * C::OROWB;
+  // Epilogue, one 32-row column block at a time: stage the block's normalised rows row-major in the
+  // wave's own LDS region (the stages are free after the last barrier; the wave reads back only what it
+  // wrote), then write whole 16-byte bf16 row pieces of O.
+  char *ob = smem + wave * 32 * C::OROWB;
   const int G = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < QB; ++j) {
     const float l = lrun[j] + __shfl_xor(lrun[j], 32, kWave);
-    const float inv = 1.0f / l;
-    char *orow = ob + (32 * j + (lane & 31)) * C::OROWB;
+    const float sc = 1.0f / l;
+    char *orow = ob + (lane & 31) * C::OROWB;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         *reinterpret_cast<floatx4 *>(orow + (hb * 32 + r4 * 8 + G * 4) * 4) =
-            floatx4{oacc[j][hb][r4 * 4 + 0] * inv, oacc[j][hb][r4 * 4 + 1] * inv, oacc[j][hb][r4 * 4 + 2] * inv,
-                    oacc[j][hb][r4 * 4 + 3] * inv};
-  }
-  // the wave reads back only what it wrote (in-order LDS within a wave)
+            floatx4{oacc[j][hb][r4 * 4 + 0] * sc, oacc[j][hb][r4 * 4 + 1] * sc, oacc[j][hb][r4 * 4 + 2] * sc,
+                    oacc[j][hb][r4 * 4 + 3] * sc};
+    const int tb = row0 + 32 * j;  // first packed row of the block
 #pragma unroll
-  for (int it = 0; it < C::QPW * HD / 8 / 64; ++it) {
-    const int c = lane + 64 * it;
-    const int ql = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
-    const int qo = m0 + ql;
-    if (qo < m_per_seq) {
-      const float *src = reinterpret_cast<const float *>(ob + ql * C::OROWB) + d0;
-      float v[8];
+    for (int it = 0; it < 32 * HD / 8 / 64; ++it) {
+      const int c = lane + 64 * it;
+      const int rl = c / (HD / 8), d0 = (c % (HD / 8)) * 8;
+      if (tb + rl < rows) {
+        const float *src = reinterpret_cast<const float *>(ob + rl * C::OROWB) + d0;
+        float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = src[e];
-      st16(o + ((size_t)b * m_per_seq + qo) * ldq + (size_t)h * HD + d0, pack16(v, (const bf16_t *)nullptr));
+        for (int e = 0; e < 8; ++e) v[e] = src[e];
+        st16(o + out_row(tb + rl) * HD + d0, pack16(v, (const bf16_t *)nullptr));
+      }
     }
   }
 }
 
 template <int HD>
-static hipError_t launch_wide(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
-                              int n_tok, int hq, int hkv, hipStream_t s) {
-  typedef WideAttnCfg<HD> C;
+static hipError_t launch_packed(const void *q, const void *kc, const void *vc, void *o, int batch, int m_per_seq,
+                                int n_tok, int hq, int hkv, hipStream_t s) {
+  typedef PackAttnCfg<HD, 1, 8> C;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-  const int qblocks = (m_per_seq + C::Q - 1) / C::Q;
-  const long long nwg = (long long)qblocks * hq * batch;
+  const int rblocks = (int)(((long long)(hq / hkv) * m_per_seq + C::R - 1) / C::R);
+  const long long nwg = (long long)batch * hkv * rblocks;
   if (nwg > (1LL << 30)) return hipErrorInvalidValue;
   const int grid = (int)((nwg + 7) / 8 * 8);
-  hipLaunchKernelGGL((attention_wide_kernel<HD>), dim3(grid), dim3(256), 0, s, (const bf16_t *)q,
-                     (const bf16_t *)kc, (const bf16_t *)vc, (bf16_t *)o, m_per_seq, n_tok, hq, hkv, qblocks,
-                     (int)nwg, scale_log2);
+  hipLaunchKernelGGL((attention_packed_kernel<HD, 1, 8>), dim3(grid), dim3(64 * C::W), 0, s, (const bf16_t *)q,
+                     (const bf16_t *)kc, (const bf16_t *)vc, (bf16_t *)o, m_per_seq, n_tok, hq, hkv, rblocks, (int)nwg,
+                     scale_log2);
   return hipGetLastError();
 }
 
@@ -683,27 +699,27 @@ static hipError_t launch_qg(const void *q, const void *kc, const void *vc, void 
 
 AttnPlan plan_attention(int dtype, int batch, int m_per_seq, int n_tok, int hq, int hkv, int hd) {
   (void)n_tok;
-  (void)hkv;
   (void)hd;
   constexpr int kCUs = 256;
-  const long long heads = (long long)hq * batch;
   if (dtype == kBF16) {
-    // The 256-query kernel once it fills the chip and its query blocks are at least 3/4 full: measured
-    // at B = 8, N = 4096, 32 heads, 1024 and 656 queries per sequence 0.84 and 0.91 of the time of the
-    // kernels below, at 328 queries (blocks 64% full) 1.08.
-    const long long qb256 = (m_per_seq + 255) / 256;
-    if (heads * qb256 >= kCUs && 4LL * m_per_seq >= 3LL * 256 * qb256) return AttnPlan{kAttnWide};
+    // The packed kernel once its 256-row blocks give at least 3/4 of a round of workgroups (measured:
+    // B = 8, N = 4096, 32 heads at 327 / 655 / 1024 queries 411 / 605 / 807 us against 430 / 748 / 1084
+    // for the 64-query kernel; the Dream full recompute, 224 workgroups, 102 against 139 us; the llada
+    // full recompute, 128 workgroups, 53 against 42 us).
+    const long long units = (long long)batch * hkv * (((long long)(hq / hkv) * m_per_seq + 255) / 256);
+    if (4 * units >= 3 * kCUs) return AttnPlan{kAttnPacked};
   }
+  // 64-query workgroups unless 32-query ones fill the chip in one round
+  const long long heads = (long long)hq * batch;
   const long long wg64 = heads * ((m_per_seq + 63) / 64), wg32 = heads * ((m_per_seq + 31) / 32);
-  if (wg64 < kCUs && wg32 <= kCUs) return AttnPlan{kAttnQG1};
-  return AttnPlan{kAttnQG2};
+  return AttnPlan{wg64 < kCUs && wg32 <= kCUs ? kAttnQG1 : kAttnQG2};
 }
 
 template <typename T, int HD>
 static hipError_t run_attention(const AttnPlan &p, const void *q, const void *kc, const void *vc, void *o, int batch,
                                 int m_per_seq, int n_tok, int hq, int hkv, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (p.kind == kAttnWide) return launch_wide<HD>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
+    if (p.kind == kAttnPacked) return launch_packed<HD>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
   }
   if (p.kind == kAttnQG1) return launch_qg<T, HD, 1>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);
   if (p.kind == kAttnQG2) return launch_qg<T, HD, 2>(q, kc, vc, o, batch, m_per_seq, n_tok, hq, hkv, s);

@@ -143,8 +143,9 @@ hipError_t launch_copy_selected(const float *p_src, float *pc, const int32_t *id
 
 // Sparse-query attention: q (B*m_per_seq x hq*hd) against K^c/V^c (B x hkv x n_tok x hd).
 // The kernel that serves a launch is chosen on the host: kAttnQG1 / kAttnQG2 = workgroups of 32 / 64
-// queries of one head with the keys split over the waves; kAttnWide = 256 queries of one head (bf16).
-enum AttnKind { kAttnQG1 = 0, kAttnQG2 = 1, kAttnWide = 2 };
+// queries of one head with the keys split over their waves; kAttnPacked (bf16) = blocks of 256 rows
+// that pack the query heads of a KV group, for launches with many rows per KV head.
+enum AttnKind { kAttnQG1 = 0, kAttnQG2 = 1, kAttnPacked = 2 };
 struct AttnPlan {
   int kind;
 };

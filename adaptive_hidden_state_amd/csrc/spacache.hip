@@ -634,8 +634,9 @@ int spa_attend(const spa_shape *shape, const void *q, int32_t m_per_seq, const v
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_out)) return SPA_ERR_ALIGN;
   const size_t ob = (size_t)D.B * m_per_seq * D.dq * D.e;
   const size_t kvb = (size_t)D.B * D.hkv * D.N * D.hd * D.e;
-  if (overlap(o_out, ob, q, ob) || overlap(o_out, ob, k_cache, kvb) || overlap(o_out, ob, v_cache, kvb))
-    return SPA_ERR_ALIAS;
+  const Span wr[1] = {{o_out, ob}};
+  const Span rd[3] = {{q, ob}, {k_cache, kvb}, {v_cache, kvb}};
+  if ((st = check_disjoint(wr, 1, rd, 3)) != SPA_OK) return st;
   const AttnPlan ap = plan_attention(D.dtype, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd);
   return hip_status(
       launch_attention(D.dtype, ap, q, k_cache, v_cache, o_out, D.B, m_per_seq, D.N, D.hq, D.hkv, D.hd, stream));

@@ -122,11 +122,12 @@ static std::string gemm_key(const char *op, int dtype, int M, int N, int K, int 
 }
 
 static std::string attn_key(const StepShape &s, int m, const AttnPlan &a) {
-  static const char *names[] = {"qg1", "qg2", "wide"};
-  static const int queries[] = {32, 64, 256};
-  char b[96];
+  static const char *names[] = {"qg1", "qg2", "packed"};
+  static const int rows[] = {32, 64, 256};  // rows of a workgroup's block (packed: rows of grp heads)
+  const long long r = a.kind == kAttnPacked ? (long long)(s.hq / s.hkv) * m : m;
+  char b[128];
   snprintf(b, sizeof b, "attn:%s:%s:hd%d:%s:%s:%s", names[a.kind], s.dtype == kF32 ? "f32" : "bf16", s.hd,
-           s.hq != s.hkv ? "gqa" : "mha", m % queries[a.kind] ? "raggedq" : "wholeq",
+           s.hq != s.hkv ? "gqa" : "mha", r % rows[a.kind] ? "raggedrows" : "wholerows",
            s.N % 32 ? "raggedkeys" : "wholekeys");
   return b;
 }

@@ -344,9 +344,19 @@ def test_layer_step_full_rank_identifier():
     s = synth.LayerShape(1, 256, 2048, 16, 16, 128, 1024, 2048, "bf16")
     _check_step(Case(s, seed=62, n_drift=40, warm="kv"), 64)
 
+def _attend(spa, shape, q, m, kc, vc, dtype):
+    """spa_attend of q against the caches; the output on the host."""
+    import torch
+    o = torch.empty(shape.batch, m, shape.n_q_heads * shape.head_dim,
+                    dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+    spa.spa_attend(shape, dev(q, dtype), m, dev(kc, dtype), dev(vc, dtype), o)
+    torch.cuda.synchronize()
+    return host(o)
+
+
 @pytest.mark.parametrize("dtype,hd,hq,hkv,n,m", ATTEND_CASES)
 def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
-    import torch
+    """spa_attend against the oracle's attention (ragged key tiles and query blocks, GQA, hd 64, fp32)."""
     spa = _lib()
     b = 2
     rng = np.random.default_rng(n + m)
@@ -354,10 +364,7 @@ def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
     kc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), dtype)
     vc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), dtype)
     shape = synth.LayerShape(b, n, 256, hq, hkv, hd, 256, 16, dtype)
-    o = torch.empty(b, m, hq * hd, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
-    spa.spa_attend(shape, dev(q, dtype), m, dev(kc, dtype), dev(vc, dtype), o)
-    torch.cuda.synchronize()
-    got = host(o)
+    got = _attend(spa, shape, q, m, kc, vc, dtype)
     for bi in range(b):
         ref = oracle.attention(q[bi].astype(np.float64), kc[bi].astype(np.float64), vc[bi].astype(np.float64))
         assert rel_l2(got[bi], ref) <= tol_for(dtype), rel_l2(got[bi], ref)
@@ -365,22 +372,16 @@ def test_attend_matches_oracle(dtype, hd, hq, hkv, n, m):
 
 @pytest.mark.parametrize("b,hd,hq,hkv,n,m", ATTEND_MANY_CASES)
 def test_attend_many_queries_matches_oracle(b, hd, hq, hkv, n, m):
-    """Enough queries per head for the 256-query bf16 kernel (B H_q ceil(m / 256) >= 256 workgroups,
-    query blocks at least 3/4 full): ragged key tiles (333, 100 keys), ragged last query blocks (450,
-    700 queries), GQA groups of 8 and 4, hd 64."""
-    import torch
+    """Enough packed rows per KV head for the 256-row blocks of the packed kernel (at least 3/4 of a
+    round of workgroups): ragged key tiles (333, 100, 2047 keys), ragged last row blocks, GQA groups of 8,
+    4 and 7, hd 64."""
     spa = _lib()
-    qb = (m + 255) // 256
-    assert b * hq * qb >= 256 and 4 * m >= 3 * 256 * qb
     rng = np.random.default_rng([n, m, hq])
     q = synth.to_storage(rng.standard_normal((b, m, hq, hd)) * 1.5, "bf16")
     kc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), "bf16")
     vc = synth.to_storage(rng.standard_normal((b, hkv, n, hd)), "bf16")
     shape = synth.LayerShape(b, n, 256, hq, hkv, hd, 256, 16, "bf16")
-    o = torch.empty(b, m, hq * hd, dtype=torch.bfloat16, device="cuda")
-    spa.spa_attend(shape, dev(q, "bf16"), m, dev(kc, "bf16"), dev(vc, "bf16"), o)
-    torch.cuda.synchronize()
-    got = host(o)
+    got = _attend(spa, shape, q, m, kc, vc, "bf16")
     for bi in (0, b - 1):
         ref = oracle.attention(q[bi].astype(np.float64), kc[bi].astype(np.float64), vc[bi].astype(np.float64))
         assert rel_l2(got[bi], ref) <= tol_for("bf16"), rel_l2(got[bi], ref)
