@@ -90,8 +90,10 @@ def measured_traffic(kernel, workload):
 
 
 def summarize_profile(trace_csv=None, counter_csvs=()):
-    """Text summary of rocprofv3 CSV output: per (kernel, grid) dispatch count and average/median
-    duration from a --kernel-trace run, and per (kernel, grid) average counter values from --pmc runs."""
+    """Text summary of rocprofv3 CSV output: per (kernel, grid, phase) dispatch count and average /
+    median duration from a --kernel-trace run, and per (kernel, grid, phase) average counter values from
+    --pmc runs. phase: "step" for dispatches after a Top-k (the cached step), "full" after a cosine pass
+    without one (the full recompute, or spa_identify), "-" before either; in dispatch order."""
     import csv
     import statistics
 
@@ -107,29 +109,44 @@ def summarize_profile(trace_csv=None, counter_csvs=()):
         wg = int(row["Workgroup_Size_X"]) * int(row["Workgroup_Size_Y"]) * int(row["Workgroup_Size_Z"])
         return g, wg
 
+    def phased(rows):
+        """(row, phase) in dispatch order."""
+        phase, out = "-", []
+        for row in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            name = short(row["Kernel_Name"])
+            if name.startswith(("cosine_topk_kernel", "topk_kernel")):
+                phase = "step"
+            elif name.startswith("proxy_cosine_kernel"):
+                phase = "full"
+            out.append((row, phase))
+        return out
+
     out = []
     if trace_csv:
         groups = {}
         with open(trace_csv) as f:
-            for row in csv.DictReader(f):
+            for row, phase in phased(list(csv.DictReader(f))):
                 g, wg = grid_of(row)
                 dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
-                groups.setdefault((short(row["Kernel_Name"]), g // wg, wg), []).append(dur)
-        out.append(f"{'kernel':64s} {'workgroups':>10s} {'wg':>5s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s}")
-        for (name, nwg, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-            out.append(f"{name[:64]:64s} {nwg:10d} {wg:5d} {len(v):6d} {sum(v) / len(v):9.2f} "
+                groups.setdefault((short(row["Kernel_Name"]), g // wg, wg, phase), []).append(dur)
+        out.append(f"{'kernel':58s} {'workgroups':>10s} {'wg':>5s} {'phase':>5s} {'calls':>6s} {'avg_us':>9s} "
+                   f"{'med_us':>9s}")
+        for (name, nwg, wg, ph), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{name[:58]:58s} {nwg:10d} {wg:5d} {ph:>5s} {len(v):6d} {sum(v) / len(v):9.2f} "
                        f"{statistics.median(v):9.2f}")
     for path in counter_csvs:
         groups = {}
         with open(path) as f:
-            for row in csv.DictReader(f):
-                g, wg = grid_of(row)
-                groups.setdefault((short(row["Kernel_Name"]), g // wg, wg, row["Counter_Name"]), []).append(
-                    float(row["Counter_Value"]))
+            rows = list(csv.DictReader(f))
+        for row, phase in phased(rows):
+            g, wg = grid_of(row)
+            groups.setdefault((short(row["Kernel_Name"]), g // wg, wg, phase, row["Counter_Name"]), []).append(
+                float(row["Counter_Value"]))
         out.append("")
-        out.append(f"{'kernel':64s} {'workgroups':>10s} {'wg':>5s} {'counter':>12s} {'calls':>6s} {'avg':>14s}")
-        for (name, nwg, wg, cn), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-            out.append(f"{name[:64]:64s} {nwg:10d} {wg:5d} {cn:>12s} {len(v):6d} {sum(v) / len(v):14.1f}")
+        out.append(f"{'kernel':58s} {'workgroups':>10s} {'wg':>5s} {'phase':>5s} {'counter':>12s} {'calls':>6s} "
+                   f"{'avg':>14s}")
+        for (name, nwg, wg, ph, cn), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            out.append(f"{name[:58]:58s} {nwg:10d} {wg:5d} {ph:>5s} {cn:>12s} {len(v):6d} {sum(v) / len(v):14.1f}")
     return "\n".join(out)
 
 
