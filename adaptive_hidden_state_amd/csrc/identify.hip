@@ -29,7 +29,19 @@ __device__ __forceinline__ void cosine_row(const float *__restrict__ part, int s
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
   for (int col = lane * 4; col < r; col += 256) {
     floatx4 v = *reinterpret_cast<const floatx4 *>(part + base + col);
-    for (int sp = 1; sp < splits; ++sp) v += *reinterpret_cast<const floatx4 *>(part + sp * plane + base + col);
+    // the other splits eight at a time: the loads of a group are all in flight before the first add
+    // (one memory round trip per group instead of one per split; measured 1 us off the fused kernel
+    // at 8 splits), and the adds keep split order
+    for (int sp = 1; sp < splits; sp += 8) {
+      floatx4 t[8];
+      const int nb = min(8, splits - sp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < nb) t[j] = *reinterpret_cast<const floatx4 *>(part + (size_t)(sp + j) * plane + base + col);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < nb) v += t[j];
+    }
 #pragma unroll
     for (int x = 0; x < 4; ++x) n1 += v[x] * v[x];
     if (pc_read != nullptr) {

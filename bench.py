@@ -287,11 +287,12 @@ def base_line(args, wl, s, value, unit, ms_step, steps, warmup, data):
     }
 
 
-def timed_blocks(step, first, steps, blocks):
-    """Time exactly `steps` consecutive calls step(first), step(first + 1), ... as `blocks` consecutive
-    blocks of (nearly) equal size, with an event on the current stream between blocks and a
-    synchronize before the first and after the last. Returns the median over the blocks of the time
-    per step (ms) and the per-block values."""
+def timed_blocks(step, first, steps, blocks, run_range=None):
+    """Time exactly `steps` consecutive steps first, first + 1, ... as `blocks` consecutive blocks of
+    (nearly) equal size, with an event on the current stream between blocks and a synchronize before
+    the first and after the last; a block runs step(i) for each of its steps, or run_range(i, n) when
+    given (n steps from step i). Returns the median over the blocks of the time per step (ms) and the
+    per-block values."""
     import numpy as np
     import torch
     nb = max(1, min(blocks, steps))
@@ -301,9 +302,13 @@ def timed_blocks(step, first, steps, blocks):
     i = first
     evs[0].record()
     for b, n in enumerate(sizes):
-        for _ in range(n):
-            step(i)
-            i += 1
+        if run_range is not None:
+            run_range(i, n)
+            i += n
+        else:
+            for _ in range(n):
+                step(i)
+                i += 1
         evs[b + 1].record()
     torch.cuda.synchronize()
     per = [evs[b].elapsed_time(evs[b + 1]) / sizes[b] for b in range(nb)]
@@ -387,31 +392,46 @@ def run_layer(args, wl):
         r, j = which(i)
         spa.spa_layer_full(s, dws[r], scratch[r], xds[r][j], ws)
 
-    # one captured HIP graph per (instance, input step) for each path; every launch of a step is
-    # stream-ordered and allocation-free, so the step is capturable as is
-    graphs = capture(args, [lambda i=i: eager_step(i) for i in range(R * n_in)]) if args.graph else None
-    graphs_full = capture(args, [lambda i=i: eager_full(i) for i in range(R * n_in)]) if args.graph else None
+    # Captured HIP graphs (every launch of a step is stream-ordered and allocation-free, so a step is
+    # capturable as is): one per (instance, input step), and one per input step holding the R steps of
+    # the R instances in turn, as a denoising step's graph holds the steps of every layer. A range of
+    # steps replays the R-step graphs where whole groups fit and the one-step graphs elsewhere.
+    G = R if args.graph_group else 1
+    graphs = graphs_full = groups = groups_full = None
+    if args.graph:
+        graphs = capture(args, [lambda i=i: eager_step(i) for i in range(R * n_in)])
+        graphs_full = capture(args, [lambda i=i: eager_full(i) for i in range(R * n_in)])
+        if G > 1 and graphs is not None:
+            groups = capture(args, [lambda g=g: [eager_step(i) for i in range(g * R, g * R + R)] for g in range(n_in)])
+            groups_full = capture(args, [lambda g=g: [eager_full(i) for i in range(g * R, g * R + R)]
+                                         for g in range(n_in)])
 
-    def replay(gs, eager):
-        def run(i):
-            if gs is not None:
-                r, j = which(i)
-                gs[r * n_in + (j - 1)].replay()
-            else:
-                eager(i)
+    def replay(gs, grp, eager):
+        def run(i0, n):
+            i, end = i0, i0 + n
+            while i < end:
+                if grp is not None and i % R == 0 and i + R <= end:
+                    grp[(i // R) % n_in].replay()
+                    i += R
+                    continue
+                if gs is not None:
+                    r, j = which(i)
+                    gs[r * n_in + (j - 1)].replay()
+                else:
+                    eager(i)
+                i += 1
         return run
 
-    step, full = replay(graphs, eager_step), replay(graphs_full, eager_full)
-    for i in range(warmup):
-        step(i)
-        full(i)
+    step, full = replay(graphs, groups, eager_step), replay(graphs_full, groups_full, eager_full)
+    step(0, warmup)
+    full(0, warmup)
     torch.cuda.synchronize()
-    log(f"[bench] timing {steps} cached layer steps ({'graphs' if graphs else 'eager'}, {R} instances, "
-        f"{args.blocks} blocks)")
-    ms_step, per_step = timed_blocks(step, warmup, steps, args.blocks)
+    log(f"[bench] timing {steps} cached layer steps ({'graphs of %d steps' % (G if groups else 1) if graphs else 'eager'}, "
+        f"{R} instances, {args.blocks} blocks)")
+    ms_step, per_step = timed_blocks(None, warmup, steps, args.blocks, run_range=step)
     log(f"[bench] timing {steps} full recomputes")
-    ms_full, per_full = timed_blocks(full, warmup, steps, args.blocks)
-    del scratch, graphs_full
+    ms_full, per_full = timed_blocks(None, warmup, steps, args.blocks, run_range=full)
+    del scratch, graphs_full, groups_full
 
     # per-kernel durations: HIP events between the kernels of the same step sequence
     it = iter(range(10 ** 9))
@@ -437,10 +457,12 @@ def run_layer(args, wl):
     line["ideal_floor_ms"] = round(ideal_floor_us(work, peak_flops) / 1e3, 5)
     line["per_kernel_us"] = {n: round(v, 2) for n, v in per_us.items()}
     line["per_kernel_roofline"] = per_kernel_fractions(per_us, work, peak_flops)
-    line["timing"] = {"graphs": graphs is not None, "instances": R, **block_stats(per_step, ms_step),
+    line["timing"] = {"graphs": graphs is not None, "instances": R,
+                      "steps_per_graph": G if groups is not None else 1, **block_stats(per_step, ms_step),
                       "full_recompute": block_stats(per_full, ms_full),
-                      "note": "ms_per_step = median over the blocks of the timed steps; per-kernel us from HIP "
-                              "events recorded between kernels on the launch stream"}
+                      "note": "ms_per_step = median over the blocks of the timed steps (steps_per_graph consecutive "
+                              "steps, one per layer instance, per graph launch; the full recompute likewise); "
+                              "per-kernel us from HIP events recorded between kernels on the launch stream"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
     line["gpu"] = gpu_info()
     if not args.no_cpu_baseline:
@@ -861,6 +883,9 @@ def main():
     ap.add_argument("--instances", type=int, default=4,
                     help="independent layer instances visited in turn (defeats Infinity-Cache reuse)")
     ap.add_argument("--no-graph", dest="graph", action="store_false", help="time eager launches")
+    ap.add_argument("--graph-per-step", dest="graph_group", action="store_false",
+                    help="layer workloads: one graph launch per step (default: the steps of the R instances "
+                         "in one graph, as a denoising step's graph holds every layer)")
     ap.add_argument("--blocks", type=int, default=5,
                     help="the timed steps run as this many consecutive blocks; ms_per_step is their median")
     ap.add_argument("--budget", choices=["adaptive", "uniform"], default="adaptive",

@@ -28,8 +28,8 @@
  *     workspace) must not overlap one another nor any buffer the call only reads (h_in, the packed
  *     weights and biases, idx, the p_cache of spa_identify, the scores of spa_topk, q and K^c/V^c of
  *     spa_attend): SPA_ERR_ALIAS otherwise. Read-only buffers may overlap each other.
- *   - Threads. No global mutable state: concurrent calls on different streams with disjoint
- *     buffers are safe.
+ *   - Threads. Concurrent calls on different streams with disjoint buffers are safe, except
+ *     spa_layer_step_noalloc: its calls share one device scratch per GPU (see there).
  *   - Supported shapes: 1 <= N <= 16384; d % 64 == 0, d <= 8192 (bf16) or 4096 (fp32);
  *     d_ffn % 16 == 0; head_dim in {64, 128};
  *     n_q_heads % n_kv_heads == 0; r % 16 == 0, 16 <= r <= min(d, d_kv) (r = d_kv with W_r = W_v diag(g)
