@@ -75,8 +75,8 @@ constexpr int kBigTileCfg = 6;
 // Tile configurations of the LDS-DMA small-M kernel (bf16, no kEpiPartial): kDmaCfg0 + i for tiles
 // kDmaTiles[i] (BM x BN).
 constexpr int kDmaCfg0 = 7;
-constexpr int kDmaTileCount = 3;
-constexpr int kDmaTiles[kDmaTileCount][2] = {{128, 192}, {128, 128}, {128, 64}};
+constexpr int kDmaTileCount = 4;
+constexpr int kDmaTiles[kDmaTileCount][2] = {{128, 192}, {128, 128}, {128, 64}, {128, 96}};
 
 GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind);
 // Plan of the columns [p.n_main, N) of a column-split SwiGLU plan (p.n_main > 0), launched after the
