@@ -152,16 +152,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 }
 
 // Exclusive prefix sum over the workgroup (kTopkThreads = 512 threads, 8 waves; wsum has room for up
-// to 16 waves).
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum) {
+// to 16 waves). The _open form leaves out the closing barrier: the caller must pass another barrier
+// before anything writes wsum again.
+__device__ __forceinline__ uint32_t block_exclusive_scan_open(uint32_t v, uint32_t *wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += wsum[w];
-  __syncthreads();
   return base + x - v;
+}
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum) {
+  const uint32_t e = block_exclusive_scan_open(v, wsum);
+  __syncthreads();
+  return e;
 }
 
 // AND / OR over a wave: rotations inside each 16-lane row (DPP row_ror), then the four row results.
@@ -271,7 +276,9 @@ __device__ void topk_block(const float *s, int n, int k, int32_t *out, TopkShare
       hn[BPT * tid + q] = 0u;
       tot += v[q];
     }
-    uint32_t e = block_exclusive_scan(tot, wsum);
+    // three barriers per pass: the wsum reads of this scan and the sel_* reads below end before the
+    // next pass's histogram barrier, the first point where wsum and sel_* are written again
+    uint32_t e = block_exclusive_scan_open(tot, wsum);
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
       const uint32_t i1 = e + v[q];
@@ -286,7 +293,6 @@ __device__ void topk_block(const float *s, int n, int k, int32_t *out, TopkShare
     prefix = sel_prefix;
     krem = sel_krem;
     full = sel_full != 0u;
-    __syncthreads();
     hi = lo - 1;
     ++pass;
     if (full) break;

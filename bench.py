@@ -393,25 +393,26 @@ def run_layer(args, wl):
         spa.spa_layer_full(s, dws[r], scratch[r], xds[r][j], ws)
 
     # Captured HIP graphs (every launch of a step is stream-ordered and allocation-free, so a step is
-    # capturable as is): one per (instance, input step), and one per input step holding the R steps of
-    # the R instances in turn, as a denoising step's graph holds the steps of every layer. A range of
-    # steps replays the R-step graphs where whole groups fit and the one-step graphs elsewhere.
+    # capturable as is): one per (instance, input step), and one per window of R consecutive steps
+    # (the R instances in turn, from any starting step), as a denoising step's graph holds the steps of
+    # every layer. Step i's work depends only on i mod R n_in. A range of steps replays the R-step
+    # graphs while whole windows fit and the one-step graphs for the rest.
     G = R if args.graph_group else 1
+    period = R * n_in
     graphs = graphs_full = groups = groups_full = None
     if args.graph:
-        graphs = capture(args, [lambda i=i: eager_step(i) for i in range(R * n_in)])
-        graphs_full = capture(args, [lambda i=i: eager_full(i) for i in range(R * n_in)])
+        graphs = capture(args, [lambda i=i: eager_step(i) for i in range(period)])
+        graphs_full = capture(args, [lambda i=i: eager_full(i) for i in range(period)])
         if G > 1 and graphs is not None:
-            groups = capture(args, [lambda g=g: [eager_step(i) for i in range(g * R, g * R + R)] for g in range(n_in)])
-            groups_full = capture(args, [lambda g=g: [eager_full(i) for i in range(g * R, g * R + R)]
-                                         for g in range(n_in)])
+            groups = capture(args, [lambda w=w: [eager_step(i) for i in range(w, w + R)] for w in range(period)])
+            groups_full = capture(args, [lambda w=w: [eager_full(i) for i in range(w, w + R)] for w in range(period)])
 
     def replay(gs, grp, eager):
         def run(i0, n):
             i, end = i0, i0 + n
             while i < end:
-                if grp is not None and i % R == 0 and i + R <= end:
-                    grp[(i // R) % n_in].replay()
+                if grp is not None and i + R <= end:
+                    grp[i % period].replay()
                     i += R
                     continue
                 if gs is not None:
