@@ -242,6 +242,26 @@ def per_kernel_fractions(per_us, work, peak_flops):
     return out
 
 
+IDENTIFY_KERNELS = ("proxy_gemm", "cosine_topk", "proxy_cosine", "topk")
+
+
+def identification_summary(per_us, work, ms_step, target_us=None):
+    """The update identification (proxy projection, cosine, Top-k) against its roofline target: its
+    event-bracketed time, share of the step, algorithmic bytes and the fraction of HBM peak they
+    reach (target 0.6); target_us: a time target for the whole identification, if one applies."""
+    names = [n for n in IDENTIFY_KERNELS if n in per_us and n in work]
+    if not names:
+        return None
+    us = sum(per_us[n] for n in names)
+    byts = sum(work[n][0] for n in names)
+    out = {"kernels": names, "us": round(us, 2), "share_of_step": round(us / (ms_step * 1e3), 4),
+           "algorithmic_bytes": byts, "GB/s": round(byts / us / 1e3, 1),
+           "hbm_frac": round(byts / us / 1e3 / PEAK_HBM_GBS, 4), "hbm_frac_target": 0.6}
+    if target_us is not None:
+        out["target_us"] = target_us
+    return out
+
+
 def dominant_roofline(per_us, work, peak_flops, workload):
     """Roofline of the longest GEMM (the dominant kernel of every workload here)."""
     dom = max((n for n in per_us if n in work and n in GEMM_KERNELS), key=lambda n: per_us[n])
@@ -407,23 +427,8 @@ def run_layer(args, wl):
             groups = capture(args, [lambda w=w: [eager_step(i) for i in range(w, w + R)] for w in range(period)])
             groups_full = capture(args, [lambda w=w: [eager_full(i) for i in range(w, w + R)] for w in range(period)])
 
-    def replay(gs, grp, eager):
-        def run(i0, n):
-            i, end = i0, i0 + n
-            while i < end:
-                if grp is not None and i + R <= end:
-                    grp[i % period].replay()
-                    i += R
-                    continue
-                if gs is not None:
-                    r, j = which(i)
-                    gs[r * n_in + (j - 1)].replay()
-                else:
-                    eager(i)
-                i += 1
-        return run
-
-    step, full = replay(graphs, groups, eager_step), replay(graphs_full, groups_full, eager_full)
+    step = range_runner(graphs, groups, eager_step, R, n_in)
+    full = range_runner(graphs_full, groups_full, eager_full, R, n_in)
     step(0, warmup)
     full(0, warmup)
     torch.cuda.synchronize()
@@ -465,6 +470,7 @@ def run_layer(args, wl):
                               "steps, one per layer instance, per graph launch; the full recompute likewise); "
                               "per-kernel us from HIP events recorded between kernels on the launch stream"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["identification"] = identification_summary(per_us, work, ms_step, 10.0 if wl.name == "llada-layer" else None)
     line["gpu"] = gpu_info()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -475,6 +481,28 @@ def run_layer(args, wl):
     else:
         line["cpu_baseline"] = None
     return line
+
+
+def range_runner(single, windows, eager, R, n_in):
+    """run(i0, n): steps i0 .. i0 + n - 1 of the rotation (step i = instance i mod R at input step
+    1 + (i div R) mod n_in, which depends only on i mod R n_in), replaying windows[i mod R n_in] (a graph
+    of steps i .. i + R - 1) while a whole window fits, else single[i mod R n_in] (a graph of step i),
+    else eager(i)."""
+    period = R * n_in
+
+    def run(i0, n):
+        i, end = i0, i0 + n
+        while i < end:
+            if windows is not None and i + R <= end:
+                windows[i % period].replay()
+                i += R
+                continue
+            if single is not None:
+                single[i % period].replay()
+            else:
+                eager(i)
+            i += 1
+    return run
 
 
 def capture(args, fns):
@@ -672,6 +700,7 @@ def run_stack(args, wl):
                       "note": "ms_per_step = median over the blocks of one denoising step through all layers (the "
                               "unmasking copy included); per-kernel us summed over the layers of one step"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["identification"] = identification_summary(per_us, work, ms_step)
     line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
@@ -832,6 +861,7 @@ def run_batched(args, wl):
                       "note": "eager launches (steps of milliseconds); every ms_per_step is the median over the "
                               "blocks of its timed steps; per-kernel us at the headline point"}
     line["roofline"] = dominant_roofline(per_us, work, peak_flops, wl.name)
+    line["identification"] = identification_summary(per_us, work, ms_step)
     line["gpu"] = gpu_info()
     line["cpu_baseline"] = None
     if not args.no_cpu_baseline:
