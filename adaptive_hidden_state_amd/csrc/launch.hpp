@@ -75,6 +75,8 @@ constexpr int kBigTileCfg = 6;
 // Tile configurations of the LDS-DMA small-M kernel (bf16, no kEpiPartial): kDmaCfg0 + i for tiles
 // kDmaTiles[i] (BM x BN).
 constexpr int kDmaCfg0 = 7;
+// The proxy projection's own kernel (bf16, kEpiPartial, N = 128): 32-row x 128-column tiles, split-K.
+constexpr int kProxyCfg = 16;
 constexpr int kDmaTileCount = 4;
 constexpr int kDmaTiles[kDmaTileCount][2] = {{128, 192}, {128, 128}, {128, 64}, {128, 96}};
 

@@ -50,8 +50,14 @@ static int sweep() {
             ++plans;
             if (p.n_main != 0) ++splits_n;
             const bool big = p.cfg == kBigTileCfg, dma = p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount;
+            const bool proxy = p.cfg == kProxyCfg;
             int bm = 0, bn = 0;
-            if (big) {
+            if (proxy) {
+              bm = 32;
+              bn = 128;
+              if (dtype != kBF16 || kind != kEpiPartial || N != 128)
+                fail("proxy kernel outside the bf16 rank-128 projection", dtype, M, N, K, kind, p);
+            } else if (big) {
               bm = bn = 256;
             } else if (dma) {
               bm = kDmaTiles[p.cfg - kDmaCfg0][0];
@@ -98,7 +104,9 @@ static int sweep() {
 // ---------------------------------------------------------------------------------------------
 static std::string tile_name(int dtype, const GemmPlan &p) {
   char b[64];
-  if (p.cfg == kBigTileCfg)
+  if (p.cfg == kProxyCfg)
+    snprintf(b, sizeof b, "proxy%dx%d", p.bm, p.bn);
+  else if (p.cfg == kBigTileCfg)
     snprintf(b, sizeof b, "big256x256");
   else if (p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount)
     snprintf(b, sizeof b, "dma%dx%d", p.bm, p.bn);
