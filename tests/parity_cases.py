@@ -17,7 +17,14 @@ FUSED_TOPK_SHAPES = [SMALL_BF16[0], SMALL_BF16[1],
                      synth.LayerShape(5, 3, 128, 2, 2, 64, 256, 16, "bf16"),
                      synth.LayerShape(3, 1030, 256, 4, 4, 64, 688, 32, "bf16"),
                      synth.LayerShape(2, 3000, 256, 4, 4, 64, 688, 32, "bf16"),
-                     synth.LayerShape(1, 4100, 256, 4, 4, 64, 688, 32, "bf16")]
+                     synth.LayerShape(1, 4100, 256, 4, 4, 64, 688, 32, "bf16"),
+                     # rank 128 (the projection on 32-row tiles): tiles shared by sequences, several
+                     # sequences completing in one workgroup of the cosine kernel
+                     synth.LayerShape(5, 3, 128, 2, 2, 64, 256, 128, "bf16"),
+                     synth.LayerShape(7, 45, 128, 2, 2, 64, 256, 128, "bf16"),
+                     synth.LayerShape(3, 1030, 256, 4, 4, 64, 688, 128, "bf16"),
+                     synth.LayerShape(2, 1500, 256, 4, 4, 64, 688, 128, "bf16"),
+                     synth.LayerShape(1, 4000, 256, 4, 4, 64, 688, 128, "bf16")]
 
 
 def fused_topk_ks(n):
