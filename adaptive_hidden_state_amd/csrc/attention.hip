@@ -106,24 +106,10 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int qg = wave % kAttnQG, kr = wave / kAttnQG;
-  const int m0 = qb * kAttnQueries + qg * 32;
   const int ldq = hq * HD;
   auto stage = [&](int buf) { return smem + ((C::NBUF > 1 ? buf : 0) * KR + kr) * C::STAGE; };
 
-  // Q fragments: B operand of S^T = K Q^T (column = query lane%32, k = head dim).
-  FragT qf[QSTEPS];
-  {
-    const int qrow = min(m0 + (lane & 31), m_per_seq - 1);
-    const T *qp = q + ((size_t)b * m_per_seq + qrow) * ldq + (size_t)h * HD;
-#pragma unroll
-    for (int st = 0; st < QSTEPS; ++st) {
-      if constexpr (BF)
-        qf[st] = ld16(qp + st * 16 + (lane >> 5) * 8);
-      else
-        qf[st] = qp[st * 2 + (lane >> 5)];
-    }
-  }
-
+  FragT qf[QSTEPS];  // Q fragments (filled below, once the first tile's loads are out)
   const size_t head_off = ((size_t)b * hkv + g) * (size_t)n_tok * HD;
   const T *kbase = kc + head_off;
   const T *vbase = vc + head_off;
@@ -305,9 +291,44 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     }
   };
 
+  // Q fragments: B operand of S^T = K Q^T (column = query lane%32, k = head dim). The KR waves of a
+  // query group need the same fragments: the workgroup loads its Q block from memory once, each thread
+  // a share of its 16-byte chunks, into LDS (rows of QROWB bytes at the start of the stage area, free
+  // until the first tile store), and every wave reads its fragments from there. The first tile's loads
+  // go out before the Q block lands.
+  constexpr int QROWB = HD * (int)sizeof(T) + 16;
+  constexpr int QCH = HD * (int)sizeof(T) / 16;            // 16-byte chunks per query row
+  static_assert(C::Q * QROWB <= C::LDS, "Q block in the stage area");
+  {
+    u32x4 qc[(C::Q * QCH + 64 * C::W - 1) / (64 * C::W)];
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(qc) / sizeof(qc[0])); ++j) {
+      const int c = tid + j * 64 * C::W;
+      if (c < C::Q * QCH) {
+        const int qrow = min(qb * kAttnQueries + c / QCH, m_per_seq - 1);
+        qc[j] = ld16(q + ((size_t)b * m_per_seq + qrow) * ldq + (size_t)h * HD + (c % QCH) * VEC);
+      }
+    }
+    gload(t_begin);
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(qc) / sizeof(qc[0])); ++j) {
+      const int c = tid + j * 64 * C::W;
+      if (c < C::Q * QCH) st16(smem + (c / QCH) * QROWB + (c % QCH) * 16, qc[j]);
+    }
+    __syncthreads();
+    const char *qrow = smem + (qg * 32 + (lane & 31)) * QROWB;
+#pragma unroll
+    for (int st = 0; st < QSTEPS; ++st) {
+      if constexpr (BF)
+        qf[st] = *reinterpret_cast<const u32x4 *>(qrow + (st * 16 + (lane >> 5) * 8) * 2);
+      else
+        qf[st] = *reinterpret_cast<const float *>(qrow + (st * 2 + (lane >> 5)) * 4);
+    }
+    __syncthreads();  // every wave holds its fragments before the first tile store overwrites the block
+  }
+
   // Tile i + 1 is loaded into registers during tile i and written to the (other) stage after it; with
   // shared stages one barrier per tile (every wave runs the same tper tiles).
-  gload(t_begin);
   lstore(0);
   gload(t_begin + 1);
   if constexpr (QG > 1) __syncthreads();

@@ -88,6 +88,51 @@ __device__ __forceinline__ void rope8(float *v, int pos, int e, int hd, float lo
   }
 }
 
+// The two residual epilogues in two steps, so that the split-K reduce can issue its loads before any
+// of them lands. resid_load8: the raw token index of row m and the raw residual row (kEpiResid: source
+// row b n_tok + i, i clamped, which needs the index first; kEpiResidScatter: row m, loaded whether or
+// not the row is written). Without an update set the index load reads a harmless word at `any` and is
+// ignored, so no load sits under a branch. resid_store8: r = residual + v and the store (kEpiResid: row
+// m of out, with the sum of squares of the stored values; kEpiResidScatter: H^c row b n_tok + i,
+// skipped out of range).
+template <typename T> struct Raw8 {
+  u32x4 w[sizeof(T) / 2];
+  int32_t idx;
+};
+template <typename T, int KIND>
+__device__ __forceinline__ void resid_load8(const EpiArgs &ea, int m, int n0, const void *any, Raw8<T> &raw) {
+  raw.idx = *(ea.idx != nullptr ? ea.idx + m : reinterpret_cast<const int32_t *>(any));
+  const T *src = (const T *)ea.src + n0;
+  if constexpr (KIND == kEpiResid) {
+    const int b = m / ea.k_per_seq;
+    const int i = ea.idx != nullptr ? raw.idx : m - b * ea.k_per_seq;
+    src += ((size_t)b * ea.n_tok + min(max(i, 0), ea.n_tok - 1)) * ea.ld_src;
+  } else {
+    src += (size_t)m * ea.ld_src;
+  }
+#pragma unroll
+  for (int h = 0; h < (int)(sizeof(T) / 2); ++h) raw.w[h] = ld16(src + h * (8 / (sizeof(T) / 2)));
+}
+template <typename T, int KIND>
+__device__ __forceinline__ void resid_store8(const EpiArgs &ea, int m, int n0, const Raw8<T> &raw, const float *v,
+                                             float *ssq) {
+  const int b = m / ea.k_per_seq;
+  const int i = ea.idx != nullptr ? raw.idx : m - b * ea.k_per_seq;
+  if constexpr (KIND == kEpiResidScatter)
+    if ((unsigned)i >= (unsigned)ea.n_tok) return;
+  float r[8];
+#pragma unroll
+  for (int h = 0; h < (int)(sizeof(T) / 2); ++h) unpack16(raw.w[h], r + h * (8 / (sizeof(T) / 2)), (const T *)nullptr);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) r[x] += v[x];
+  if constexpr (KIND == kEpiResid) {
+    store8((T *)ea.out + (size_t)m * ea.ldo + n0, r);
+    if (ssq != nullptr) *ssq = stored_sq8<T>(r);
+  } else {
+    store8((T *)ea.out + ((size_t)b * ea.n_tok + i) * ea.ldo + n0, r);
+  }
+}
+
 template <typename T, int KIND>
 __device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const float *v, float *ssq = nullptr) {
   if constexpr (KIND == kEpiQKV) {
@@ -119,25 +164,10 @@ __device__ __forceinline__ void epi8(const EpiArgs &ea, int m, int n0, const flo
     const int g = nn / ea.hd, e = nn - g * ea.hd;
     if (is_k && rope) rope8(w8, i, e, ea.hd, ea.rope_log2_theta);
     store8(dst + (((size_t)b * ea.hkv + g) * ea.n_tok + i) * ea.hd + e, w8);
-  } else if constexpr (KIND == kEpiResid) {
-    int b;
-    int i = map_token(ea, m, b);
-    i = min(max(i, 0), ea.n_tok - 1);
-    float r[8];
-    load8((const T *)ea.src + ((size_t)b * ea.n_tok + i) * ea.ld_src + n0, r);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) r[x] += v[x];
-    store8((T *)ea.out + (size_t)m * ea.ldo + n0, r);
-    if (ssq != nullptr) *ssq = stored_sq8<T>(r);
-  } else if constexpr (KIND == kEpiResidScatter) {
-    int b;
-    const int i = map_token(ea, m, b);
-    if ((unsigned)i >= (unsigned)ea.n_tok) return;
-    float r[8];
-    load8((const T *)ea.src + (size_t)m * ea.ld_src + n0, r);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) r[x] += v[x];
-    store8((T *)ea.out + ((size_t)b * ea.n_tok + i) * ea.ldo + n0, r);
+  } else if constexpr (KIND == kEpiResid || KIND == kEpiResidScatter) {
+    Raw8<T> raw;
+    resid_load8<T, KIND>(ea, m, n0, v, raw);
+    resid_store8<T, KIND>(ea, m, n0, raw, v, ssq);
   } else if constexpr (KIND == kEpiPartial) {
     store8((float *)ea.out + (size_t)m * ea.ldo + n0, v);
   }
@@ -980,8 +1010,46 @@ __global__ __launch_bounds__(512) void gemm_dma_kernel(const bf16_t *__restrict_
   }
 }
 
+// v[0..7] (+)= the sum over S consecutive splits of p[s plane + 0..7], added in split order; all S
+// loads are issued before the first addition.
+template <int S>
+__device__ __forceinline__ void add_partials8(const float *p, size_t plane, float *v) {
+  floatx4 a[S][2];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    a[j][0] = *reinterpret_cast<const floatx4 *>(p + (size_t)j * plane);
+    a[j][1] = *reinterpret_cast<const floatx4 *>(p + (size_t)j * plane + 4);
+  }
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      v[x] += a[j][0][x];
+      v[4 + x] += a[j][1][x];
+    }
+}
+// v[0..7] = the sum over the splits s of p[s plane + 0..7], added in split order from zero
+// (deterministic), up to eight splits' loads in flight together.
+__device__ __forceinline__ void sum_partials8(const float *p, size_t plane, int splits, float *v) {
+#pragma unroll
+  for (int x = 0; x < 8; ++x) v[x] = 0.f;
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) add_partials8<8>(p + (size_t)s * plane, plane, v);
+  switch (splits - s) {
+    case 1: add_partials8<1>(p + (size_t)s * plane, plane, v); break;
+    case 2: add_partials8<2>(p + (size_t)s * plane, plane, v); break;
+    case 3: add_partials8<3>(p + (size_t)s * plane, plane, v); break;
+    case 4: add_partials8<4>(p + (size_t)s * plane, plane, v); break;
+    case 5: add_partials8<5>(p + (size_t)s * plane, plane, v); break;
+    case 6: add_partials8<6>(p + (size_t)s * plane, plane, v); break;
+    case 7: add_partials8<7>(p + (size_t)s * plane, plane, v); break;
+    default: break;
+  }
+}
+
 // Sum of the split-K partials in split order (deterministic), then the epilogue, eight columns (or
-// eight hidden units) per thread.
+// eight hidden units) per thread. The residual epilogues issue their token-index and residual loads
+// before the partial loads, so each thread waits about one memory round trip.
 template <typename T, int KIND>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int splits, int M,
                                                             int N, EpiArgs ea) {
@@ -992,17 +1060,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     if (t >= (size_t)M * f8) return;
     const int m = (int)(t / f8), j0 = (int)(t - (size_t)m * f8) * 8;
     const int ng = (j0 >> 4) * 32 + (j0 & 15);
-    float g[8] = {}, u[8] = {};
-    for (int s = 0; s < splits; ++s) {
-      float a[8], c[8];
-      load8(part + s * plane + (size_t)m * N + ng, a);
-      load8(part + s * plane + (size_t)m * N + ng + 16, c);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        g[x] += a[x];
-        u[x] += c[x];
-      }
-    }
+    float g[8], u[8];
+    sum_partials8(part + (size_t)m * N + ng, plane, splits, g);
+    sum_partials8(part + (size_t)m * N + ng + 16, plane, splits, u);
     epi8_swiglu<T>(ea, m, j0, g, u);
   } else {
     const int n8 = N / 8;
@@ -1011,14 +1071,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     const int m = (int)(tc / n8), n0 = (int)(tc - (size_t)m * n8) * 8;
     float ss = 0.f;
     if (valid) {
-      float v[8] = {};
-      for (int s = 0; s < splits; ++s) {
-        float a[8];
-        load8(part + s * plane + (size_t)m * N + n0, a);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) v[x] += a[x];
+      float v[8];
+      if constexpr (KIND == kEpiResid || KIND == kEpiResidScatter) {
+        Raw8<T> raw;
+        resid_load8<T, KIND>(ea, m, n0, part, raw);
+        sum_partials8(part + (size_t)m * N + n0, plane, splits, v);
+        resid_store8<T, KIND>(ea, m, n0, raw, v, &ss);
+      } else {
+        sum_partials8(part + (size_t)m * N + n0, plane, splits, v);
+        epi8<T, KIND>(ea, m, n0, v, &ss);
       }
-      epi8<T, KIND>(ea, m, n0, v, &ss);
     }
     // N % 32 == 0, so threads t & ~3 .. t | 3 hold the four chunks of one 32-column block
     if constexpr (KIND == kEpiResid)
