@@ -8,12 +8,14 @@
 // of QG = 1 but halves the number of workgroups; the launcher takes QG = 2 unless that would leave CUs
 // idle while QG = 1 fills them in one round. Each wave runs an online softmax over its range; the KR
 // partial results (running max, running sum, unnormalised output) of a query group are merged through
-// LDS at the end. K is staged as [key][hd] and V
-// transposed to [hd][key], so that both products read contiguous LDS. A wave computes S^T = K Q^T
-// (keys x queries) on 32x32 MFMA blocks; in that layout a lane holds the scores of one query, so the
-// softmax (fp32, base-2 exponent) needs one cross-lane step, and the probabilities feed O^T = V^T P^T
-// straight from registers. V is transposed on the way into LDS: a lane loads an 8-key x 8-dim block
-// (eight 16-byte row pieces), transposes it in registers and writes eight 16-byte rows of V^T.
+// LDS at the end. K and (bf16) V are staged as [key][hd] rows, copied as loaded. A wave computes
+// S^T = K Q^T (keys x queries) on 32x32 MFMA blocks; in that layout a lane holds the scores of one
+// query, so the softmax (fp32, base-2 exponent) needs one cross-lane step, and the probabilities feed
+// O^T = V^T P^T straight from registers. The V^T operand of that product (eight keys of one head dim
+// per lane) comes out of the [key][hd] rows through the LDS transpose read (ds_read_b64_tr_b16: in
+// each group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces that lanes i / 4,
+// i / 4 + 4, i / 4 + 8 and i / 4 + 12 address), two reads per fragment. fp32 V is transposed on the
+// way into LDS instead: a lane loads a 4-key x 4-dim block and writes four 16-byte rows of V^T.
 //
 // Workgroup ids are remapped so that each XCD (which receives every eighth workgroup) runs a
 // contiguous range of (sequence, KV head, query head, query block): the blocks that read the same K/V
@@ -42,13 +44,23 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 *in, u32x4 *out) {
   }
 }
 
+// ds_read_b64_tr_b16 at byte address p of LDS (see the kernel comment for its lane layout).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s *)(__attribute__((address_space(3))) const char *)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
 template <typename T, int HD, int QG> struct AttnCfg {
   static constexpr int Q = 32 * QG;                                // queries per workgroup
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int KT = 32;                                    // keys per tile
   static constexpr int KROWB = HD * (int)sizeof(T) + 16;           // K tile row stride (bytes)
-  static constexpr int VROWB = KT * (int)sizeof(T) + 16;           // V^T tile row stride (bytes)
-  static constexpr int STAGE = KT * KROWB + HD * VROWB;            // one K + V^T tile
+  // bf16: V stays [key][hd] (rows padded by 64 bytes, so the four keys of a transposed fragment read
+  // sit on disjoint banks); fp32: V^T [hd][key]
+  static constexpr int VROWB = BF ? HD * 2 + 64 : KT * (int)sizeof(T) + 16;
+  static constexpr int STAGE = KT * KROWB + (BF ? KT : HD) * VROWB;  // one K + V tile
   // Shared stages (QG > 1) are double-buffered with a barrier per tile; a key range owned by a single
   // wave (QG = 1) has one private stage and needs no barrier (a wave's LDS accesses are in order).
   static constexpr int NBUF = QG > 1 ? 2 : 1;
@@ -127,19 +139,18 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
   const int tper = (ntiles + KR - 1) / KR;
   const int t_begin = kr * tper;
 
-  // The QG waves of a key range split the tile loads: K chunks lane + 64 (j * QG + qg); V blocks
-  // qg * VW + lane + 64 p, block v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so
-  // the lanes that write one V^T row segment hold consecutive key blocks (conflict-free LDS).
-  u32x4 rk[KCH], rv[VPER][VB];
-  // This lane's element offsets inside a tile (constant over the tiles): K chunk j covers key row
-  // c / (HD / VEC), chunk c % (HD / VEC); V block p covers keys kb VB .. kb VB + VB - 1 of dim chunk cc.
-  // (row = offset / HD, column = offset % HD: HD is a power of two)
-  int koff[KCH], voff[VPER];
-#pragma unroll
-  for (int j = 0; j < KCH; ++j) {
-    const int c = lane + 64 * (j * kAttnQG + qg);
-    koff[j] = (c / (HD / VEC)) * HD + (c % (HD / VEC)) * VEC;
-  }
+  // The QG waves of a key range split the tile loads: K (and bf16 V) chunks c = lane + 64 (j QG + qg),
+  // i.e. key row krow0 + KRS j, 16-byte chunk kcol0 of the row (64 QG chunks are KRS whole rows, so
+  // the offsets of a lane's chunks differ by constants); fp32 V blocks qg * VW + lane + 64 p, block
+  // v -> key block kb = v % (KT / VB), dim chunk cc = v / (KT / VB), so the lanes that write one V^T
+  // row segment hold consecutive key blocks (conflict-free LDS).
+  u32x4 rk[KCH], rvr[BF ? KCH : 1], rv[BF ? 1 : VPER][VB];  // K rows; V rows (bf16) or V blocks (fp32)
+  constexpr int KRS = 64 * kAttnQG / (HD / VEC);
+  static_assert(64 * kAttnQG % (HD / VEC) == 0, "whole rows per load pass");
+  const int krow0 = (lane + 64 * qg) / (HD / VEC), kcol0 = (lane + 64 * qg) % (HD / VEC);
+  const int koff0 = krow0 * HD + kcol0 * VEC;  // element offset of chunk j = 0 in a tile
+  // fp32 V block p covers keys kb VB .. kb VB + VB - 1 of dim chunk cc (element offset voff[p])
+  int voff[VPER];
 #pragma unroll
   for (int p = 0; p < VPER; ++p) {
     const int v = min(qg * VW + min(lane + 64 * p, VW - 1), VTASKS - 1);
@@ -153,46 +164,48 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     const T *vt = vbase + (size_t)key0 * HD;
     if (key0 + KT <= n_tok) {  // uniform: the whole tile lies inside the keys
 #pragma unroll
-      for (int j = 0; j < KCH; ++j) rk[j] = ld16(kt + koff[j]);
+      for (int j = 0; j < KCH; ++j) rk[j] = ld16(kt + koff0 + j * KRS * HD);
+      if constexpr (BF) {
 #pragma unroll
-      for (int p = 0; p < VPER; ++p)
+        for (int j = 0; j < KCH; ++j) rvr[j] = ld16(vt + koff0 + j * KRS * HD);
+      } else {
 #pragma unroll
-        for (int j = 0; j < VB; ++j) rv[p][j] = ld16(vt + voff[p] + j * HD);
+        for (int p = 0; p < VPER; ++p)
+#pragma unroll
+          for (int j = 0; j < VB; ++j) rv[p][j] = ld16(vt + voff[p] + j * HD);
+      }
     } else {  // a tile reaching past the last key (or wholly past it, in a short key range): rows past
               // the end read the last key and are masked later
 #pragma unroll
       for (int j = 0; j < KCH; ++j) {
-        const int key = min(key0 + koff[j] / HD, n_tok - 1);
-        rk[j] = ld16(kbase + (size_t)key * HD + koff[j] % HD);
+        const int key = min(key0 + krow0 + j * KRS, n_tok - 1);
+        rk[j] = ld16(kbase + (size_t)key * HD + kcol0 * VEC);
+        if constexpr (BF) rvr[j] = ld16(vbase + (size_t)key * HD + kcol0 * VEC);
       }
+      if constexpr (!BF) {
 #pragma unroll
-      for (int p = 0; p < VPER; ++p)
+        for (int p = 0; p < VPER; ++p)
 #pragma unroll
-        for (int j = 0; j < VB; ++j) {
-          const int key = min(key0 + voff[p] / HD + j, n_tok - 1);
-          rv[p][j] = ld16(vbase + (size_t)key * HD + voff[p] % HD);
-        }
+          for (int j = 0; j < VB; ++j) {
+            const int key = min(key0 + voff[p] / HD + j, n_tok - 1);
+            rv[p][j] = ld16(vbase + (size_t)key * HD + voff[p] % HD);
+          }
+      }
     }
   };
   auto lstore = [&](int buf) {
     char *ks = stage(buf), *vts = ks + KT * KROWB;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = lane + 64 * (j * kAttnQG + qg);
-      const int row = c / (HD / VEC), col = c % (HD / VEC);
-      st16(ks + row * KROWB + col * 16, rk[j]);
+      st16(ks + (krow0 + j * KRS) * KROWB + kcol0 * 16, rk[j]);
+      if constexpr (BF) st16(vts + (krow0 + j * KRS) * VROWB + kcol0 * 16, rvr[j]);
     }
+    if constexpr (!BF) {
 #pragma unroll
-    for (int p = 0; p < VPER; ++p) {
-      const int vi = lane + 64 * p, v = qg * VW + vi;
-      if (vi >= VW || v >= VTASKS) continue;
-      const int kb = v % (KT / VB), cc = v / (KT / VB);
-      if constexpr (BF) {
-        u32x4 tr[8];
-        transpose8x8_b16(rv[p], tr);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st16(vts + (cc * 8 + e) * VROWB + kb * 16, tr[e]);
-      } else {
+      for (int p = 0; p < VPER; ++p) {
+        const int vi = lane + 64 * p, v = qg * VW + vi;
+        if (vi >= VW || v >= VTASKS) continue;
+        const int kb = v % (KT / VB), cc = v / (KT / VB);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const u32x4 col = {rv[p][0][e], rv[p][1][e], rv[p][2][e], rv[p][3][e]};
@@ -266,12 +279,16 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
         pf[1] = pack_bf16x2(s[half * 8 + 2], s[half * 8 + 3]);
         pf[2] = pack_bf16x2(s[half * 8 + 4], s[half * 8 + 5]);
         pf[3] = pack_bf16x2(s[half * 8 + 6], s[half * 8 + 7]);
-        const int c0 = (half * 16 + 4 * G) * 2, c1 = c0 + 16;
+        // A = V^T: lane l needs head dim hb 32 + l % 32 at keys half 16 + {4G..4G+3} (elements 0..3)
+        // and half 16 + 8 + {4G..4G+3} (4..7). In the transpose read, lane j of 16-lane group g
+        // addresses key half 16 + 4 (g / 2) + j / 4 (+ 8 for the second read), dims 16 (g % 2) +
+        // 4 (j % 4) .. + 3, so lane i of the group receives dim 16 (g % 2) + i at the four keys.
+        const int tg = lane >> 4, tj = lane & 15;
+        const char *vrd = vts + (half * 16 + 4 * (tg >> 1) + (tj >> 2)) * VROWB + (16 * (tg & 1) + 4 * (tj & 3)) * 2;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          const char *vrow = vts + (hb * 32 + (lane & 31)) * VROWB;
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
+          const u32x2 lo = lds_read_tr16(vrd + hb * 64);
+          const u32x2 hi = lds_read_tr16(vrd + hb * 64 + 8 * VROWB);
           const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
           oacc[hb] = mfma32(vf, pf, oacc[hb]);
         }
