@@ -32,18 +32,6 @@ template <bool BF16> struct AFrag;
 template <> struct AFrag<true> { typedef u32x4 type; };
 template <> struct AFrag<false> { typedef float type; };
 
-// 8x8 transpose of 16-bit values held as 8 rows of 8 (u32x4 each): out[e] holds column e. Each output
-// word takes one half-word from each of two rows: one v_perm_b32.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 *in, u32x4 *out) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of {row 2p, row 2p+1}
-#pragma unroll
-    for (int p = 0; p < 4; ++p) out[e][p] = __builtin_amdgcn_perm(in[2 * p + 1][w], in[2 * p][w], sel);
-  }
-}
-
 // ds_read_b64_tr_b16 at byte address p of LDS (see the kernel comment for its lane layout).
 __device__ __forceinline__ u32x2 lds_read_tr16(const char *p) {
   typedef short v4s __attribute__((ext_vector_type(4)));
@@ -448,17 +436,16 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
 template <int HD, int QB, int NW> struct PackAttnCfg {
   static constexpr int W = NW, QPW = 32 * QB, R = QPW * W;         // waves, rows per wave / per workgroup
   static constexpr int KT = 32;                                    // keys per tile
-  static constexpr int KROWB = HD * 2 + 16, VROWB = KT * 2 + 16;   // K row / V^T row strides (bytes)
-  static constexpr int STAGE = KT * KROWB + HD * VROWB;
+  // K and V rows [key][hd] as loaded; V rows padded by 64 bytes for the transposed fragment reads
+  static constexpr int KROWB = HD * 2 + 16, VROWB = HD * 2 + 64;
+  static constexpr int STAGE = KT * KROWB + KT * VROWB;
   static constexpr int OROWB = (HD + 4) * 4;                       // staged fp32 output row
   static constexpr int OUT = W * 32 * OROWB;                       // one 32-row block per wave at a time
   static constexpr int LDS = 2 * STAGE > OUT ? 2 * STAGE : OUT;
   static constexpr int KCHUNKS = KT * HD / 8;                      // K 16-byte chunks per tile
   static constexpr int KCH = (KCHUNKS + 64 * W - 1) / (64 * W);    // per lane (the last pass partial)
-  static constexpr int VTASKS = (KT / 8) * (HD / 8);               // 8x8 V blocks per tile
-  static constexpr int VW = VTASKS / W;                            // per wave (one per lane < VW)
   static_assert(QB == 1 || QB == 2, "one or two column blocks per wave");
-  static_assert((KCHUNKS % (64 * W) == 0 || KCH == 1) && VTASKS % W == 0 && VW <= 64, "tile split");
+  static_assert(KCHUNKS % (64 * W) == 0 || KCH == 1, "tile split");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -471,7 +458,7 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
                                                                    float scale_log2) {
   typedef bf16_t T;
   typedef PackAttnCfg<HD, QB, NW> C;
-  constexpr int KT = C::KT, KROWB = C::KROWB, VROWB = C::VROWB, KCH = C::KCH, VW = C::VW;
+  constexpr int KT = C::KT, KROWB = C::KROWB, VROWB = C::VROWB, KCH = C::KCH;
   constexpr int QSTEPS = HD / 16, HB = HD / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
@@ -520,18 +507,14 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
     lrun[j] = 0.f;
   }
 
-  // tile loads split over the four waves: K chunks c = lane + 64 (4 jj + wave); V block v = VW wave + lane
-  u32x4 rk[KCH], rv[8];
+  // tile loads split over the waves: K and V 16-byte chunks c = lane + 64 (W jj + wave) of the tile
+  u32x4 rk[KCH], rv[KCH];
   int koff[KCH];
 #pragma unroll
   for (int jj = 0; jj < KCH; ++jj) {
     const int c = lane + 64 * (jj * C::W + wave);
     koff[jj] = (c / (HD / 8)) * HD + (c % (HD / 8)) * 8;
   }
-  const bool vlane = lane < VW;
-  const int vtask = wave * VW + (vlane ? lane : 0);
-  const int vkb = vtask % (KT / 8), vcc = vtask / (KT / 8);
-  const int voff = vkb * 8 * HD + vcc * 8;
   // lanes past the tile's K chunks (hd 64 with eight waves) load and store none
   auto kchunk = [&](int jj) { return C::KCHUNKS % (64 * C::W) == 0 || lane + 64 * (jj * C::W + wave) < C::KCHUNKS; };
   auto gload = [&](int t) {
@@ -541,38 +524,30 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
       const T *vt = vbase + (size_t)key0 * HD;
 #pragma unroll
       for (int jj = 0; jj < KCH; ++jj)
-        if (kchunk(jj)) rk[jj] = ld16(kt + koff[jj]);
-      if (vlane) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rv[e] = ld16(vt + voff + e * HD);
-      }
+        if (kchunk(jj)) {
+          rk[jj] = ld16(kt + koff[jj]);
+          rv[jj] = ld16(vt + koff[jj]);
+        }
     } else {  // rows past the last key read the last key (masked later)
 #pragma unroll
       for (int jj = 0; jj < KCH; ++jj) {
-        const int key = min(key0 + koff[jj] / HD, n_tok - 1);
-        if (kchunk(jj)) rk[jj] = ld16(kbase + (size_t)key * HD + koff[jj] % HD);
-      }
-      if (vlane) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = min(key0 + voff / HD + e, n_tok - 1);
-          rv[e] = ld16(vbase + (size_t)key * HD + voff % HD);
+        const size_t off = (size_t)min(key0 + koff[jj] / HD, n_tok - 1) * HD + koff[jj] % HD;
+        if (kchunk(jj)) {
+          rk[jj] = ld16(kbase + off);
+          rv[jj] = ld16(vbase + off);
         }
       }
     }
   };
   auto lstore = [&](int buf) {
-    char *ks = stage(buf), *vts = ks + KT * KROWB;
+    char *ks = stage(buf), *vs = ks + KT * KROWB;
 #pragma unroll
     for (int jj = 0; jj < KCH; ++jj) {
       const int c = lane + 64 * (jj * C::W + wave);
-      if (kchunk(jj)) st16(ks + (c / (HD / 8)) * KROWB + (c % (HD / 8)) * 16, rk[jj]);
-    }
-    if (vlane) {
-      u32x4 tr[8];
-      transpose8x8_b16(rv, tr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st16(vts + (vcc * 8 + e) * VROWB + vkb * 16, tr[e]);
+      if (kchunk(jj)) {
+        st16(ks + (c / (HD / 8)) * KROWB + (c % (HD / 8)) * 16, rk[jj]);
+        st16(vs + (c / (HD / 8)) * VROWB + (c % (HD / 8)) * 16, rv[jj]);
+      }
     }
   };
 
@@ -628,10 +603,12 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
       lrun[jq] += psum;
     }
   };
-  // O^T += V^T P^T from the tile in stage buf, each V^T fragment shared by the column blocks
+  // O^T += V^T P^T from the tile in stage buf, each V^T fragment (two transposed reads of the V rows,
+  // as in attention_kernel) shared by the column blocks
   auto pv = [&](int buf, const floatx16 (&sc)[QB]) {
-    const char *vts = stage(buf) + KT * KROWB;
-    const int G = lane >> 5;
+    const char *vs = stage(buf) + KT * KROWB;
+    const int tg = lane >> 4, tj = lane & 15;
+    const char *vrd0 = vs + (4 * (tg >> 1) + (tj >> 2)) * VROWB + (16 * (tg & 1) + 4 * (tj & 3)) * 2;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       u32x4 pf[QB];
@@ -642,12 +619,11 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
         pf[jq][2] = pack_bf16x2(sc[jq][half * 8 + 4], sc[jq][half * 8 + 5]);
         pf[jq][3] = pack_bf16x2(sc[jq][half * 8 + 6], sc[jq][half * 8 + 7]);
       }
-      const int c0 = (half * 16 + 4 * G) * 2, c1 = c0 + 16;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const char *vrow = vts + (hb * 32 + (lane & 31)) * VROWB;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + c0);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + c1);
+        const char *vrd = vrd0 + half * 16 * VROWB + hb * 64;
+        const u32x2 lo = lds_read_tr16(vrd);
+        const u32x2 hi = lds_read_tr16(vrd + 8 * VROWB);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int jq = 0; jq < QB; ++jq) oacc[jq][hb] = mfma32(vf, pf[jq], oacc[jq][hb]);
