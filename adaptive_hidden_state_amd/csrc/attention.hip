@@ -230,7 +230,7 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
+    tmax = fmaxf(tmax, xor_lane<32>(tmax)) * scale_log2;
     // The exponentials are taken against a reference maximum mref that moves only when a query's
     // maximum exceeds it by more than 8 (so every p <= 2^8, safe in fp32 and in the bf16 P): the
     // running sums are rescaled rarely instead of on most tiles, and the result is the same softmax.
@@ -353,7 +353,7 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
 
   // Merge the key ranges of each query group. Every wave parks its partial state in LDS (the stages
   // are free after the last barrier), then all threads combine.
-  lrun += __shfl_xor(lrun, 32, kWave);
+  lrun += xor_lane<32>(lrun);
   {
     char *part = smem + wave * C::MERGE;
     const int G = lane >> 5;
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sc[jq][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * scale_log2;
+      tmax = fmaxf(tmax, xor_lane<32>(tmax)) * scale_log2;
       // reference maximum that moves only when a row's maximum exceeds it by more than 8 (p <= 2^8)
       const float mnew = fmaxf(mrun[jq], tmax);
       const bool grow = mnew > mrun[jq] + 8.f;
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(64 * NW) void attention_packed_kernel(const bf16_t 
   const int G = lane >> 5;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const float l = lrun[j] + __shfl_xor(lrun[j], 32, kWave);
+    const float l = lrun[j] + xor_lane<32>(lrun[j]);
     const float sc = 1.0f / l;
     char *orow = ob + (lane & 31) * C::OROWB;
 #pragma unroll

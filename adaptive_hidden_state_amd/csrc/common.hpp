@@ -87,14 +87,50 @@ __device__ __forceinline__ floatx16 mfma32(float a, float b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// The value that lane l ^ OFF of the wave holds (OFF = 1, 2, 4, 8, 16 or 32; every lane active), the
+// same exchange as __shfl_xor without its LDS round trip: DPP permutes within quads (1, 2), a half-row
+// mirror followed by a quad reversal (4), a rotation by 8 within each 16-lane row (8), and gfx950's
+// v_permlane16_swap / v_permlane32_swap across rows (16) and wave halves (32), whose two results hold
+// the pair's values in either order.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int OFF> __device__ __forceinline__ float xor_lane(float v) {
+  static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "xor offset");
+  if constexpr (OFF == 1) {
+    return dpp_mov<0xB1>(v);                 // quad_perm [1, 0, 3, 2]
+  } else if constexpr (OFF == 2) {
+    return dpp_mov<0x4E>(v);                 // quad_perm [2, 3, 0, 1]
+  } else if constexpr (OFF == 4) {
+    return dpp_mov<0x1B>(dpp_mov<0x141>(v)); // row_half_mirror, then quad_perm [3, 2, 1, 0]
+  } else if constexpr (OFF == 8) {
+    return dpp_mov<0x128>(v);                // row_ror:8
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+  }
+}
+
+// Butterfly sum / max over the wave (xor 32, 16, ..., 1): every lane ends with the same value.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  v += xor_lane<32>(v);
+  v += xor_lane<16>(v);
+  v += xor_lane<8>(v);
+  v += xor_lane<4>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<1>(v);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  v = fmaxf(v, xor_lane<32>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
   return v;
 }
 

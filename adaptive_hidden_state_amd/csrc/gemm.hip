@@ -66,8 +66,8 @@ template <> __device__ __forceinline__ float stored_sq8<bf16_t>(const float *r) 
 // threads) that handle its four 8-column chunks: every lane calls this (shuffles), valid or not.
 __device__ __forceinline__ void write_ss32(const EpiArgs &ea, int m, int n0, int N, float ss, bool valid,
                                            bool first) {
-  ss += __shfl_xor(ss, 1, kWave);
-  ss += __shfl_xor(ss, 2, kWave);
+  ss += xor_lane<1>(ss);
+  ss += xor_lane<2>(ss);
   if (valid && first) ea.ss_out[(size_t)m * (N / 32) + n0 / 32] = ss;
 }
 
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll 8
       for (int j = part_i; j < ea.ss_n / 4; j += TPR) v += ps[j];
       float t = (v[0] + v[1]) + (v[2] + v[3]);
-      if constexpr (TPR >= 2) t += __shfl_xor(t, 1, kWave);
-      if constexpr (TPR >= 4) t += __shfl_xor(t, 2, kWave);
+      if constexpr (TPR >= 2) t += xor_lane<1>(t);
+      if constexpr (TPR >= 4) t += xor_lane<2>(t);
       if (part_i == 0) row_scale[r] = 1.0f / sqrtf(t / (float)ea.norm_d + ea.norm_eps);
     }
   };
@@ -388,9 +388,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 #pragma unroll
     for (int j = 0; j < A_PER; ++j) {
       float v = ssq[j];
-      v += __shfl_xor(v, 1, kWave);
-      v += __shfl_xor(v, 2, kWave);
-      v += __shfl_xor(v, 4, kWave);
+      v += xor_lane<1>(v);
+      v += xor_lane<2>(v);
+      v += xor_lane<4>(v);
       const int m = tm * BM + ((tid + j * 256) >> 3);
       if ((tid & 7) == 0 && m < M) ea.ss_out[(size_t)split * M + m] = v;
     }
@@ -886,8 +886,8 @@ __global__ __launch_bounds__(512) void gemm_dma_kernel(const bf16_t *__restrict_
 #pragma unroll 8
       for (int j = part_i; j < ea.ss_n / 4; j += TPR) v += ps[j];
       float t = (v[0] + v[1]) + (v[2] + v[3]);
-      if constexpr (TPR >= 2) t += __shfl_xor(t, 1, kWave);
-      if constexpr (TPR >= 4) t += __shfl_xor(t, 2, kWave);
+      if constexpr (TPR >= 2) t += xor_lane<1>(t);
+      if constexpr (TPR >= 4) t += xor_lane<2>(t);
       if (part_i == 0) row_scale[r] = 1.0f / sqrtf(t / (float)ea.norm_d + ea.norm_eps);
     }
   }
@@ -1181,9 +1181,9 @@ __global__ __launch_bounds__(256) void proxy_gemm_kernel(const bf16_t *__restric
     if (m < M) pp[(size_t)m * kProxyCols] = acc[q];
   }
   if (ss_out != nullptr) {  // the 8 threads of a row add their squares in a fixed order
-    ssq += __shfl_xor(ssq, 1, kWave);
-    ssq += __shfl_xor(ssq, 2, kWave);
-    ssq += __shfl_xor(ssq, 4, kWave);
+    ssq += xor_lane<1>(ssq);
+    ssq += xor_lane<2>(ssq);
+    ssq += xor_lane<4>(ssq);
     const int m = tm * kProxyRows + arow;
     if (achunk == 0 && m < M) ss_out[(size_t)split * M + m] = ssq;
   }
