@@ -40,10 +40,11 @@ ROPE_STEP_CASES = [
 # spa_attend: (dtype, hd, hq, hkv, n keys, m queries), batch 2
 ATTEND_CASES = [("bf16", 128, 4, 4, 1024, 256), ("bf16", 64, 6, 2, 77, 13), ("f32", 64, 4, 4, 64, 16),
                 ("f32", 128, 2, 1, 100, 70), ("bf16", 128, 28, 4, 300, 65), ("bf16", 128, 28, 4, 2048, 100),
-                ("bf16", 64, 8, 8, 999, 40), ("bf16", 128, 32, 32, 1024, 51)]
+                ("bf16", 64, 8, 8, 999, 40), ("bf16", 128, 32, 32, 1024, 51),
+                ("bf16", 128, 4, 2, 20, 5), ("bf16", 64, 2, 2, 1, 3)]   # fewer keys than one tile
 # spa_attend with many packed rows per KV head (the packed kernel): (batch, hd, hq, hkv, n keys, m queries)
 ATTEND_MANY_CASES = [(8, 128, 32, 32, 333, 450), (8, 128, 32, 4, 1024, 256), (4, 64, 64, 16, 100, 700),
-                     (7, 128, 28, 4, 2047, 1000)]
+                     (7, 128, 28, 4, 2047, 1000), (8, 128, 32, 4, 24, 300)]
 
 # full-size workload layers
 LLADA_EXACT_K = [51, 87, 123, 130, 200, 256]        # LLaDA stack row counts and the workload's k
