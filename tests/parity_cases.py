@@ -48,7 +48,7 @@ ATTEND_MANY_CASES = [(8, 128, 32, 32, 333, 450), (8, 128, 32, 4, 1024, 256), (4,
 
 # full-size workload layers
 LLADA_EXACT_K = [51, 87, 123, 130, 200, 256]        # LLaDA stack row counts and the workload's k
-DREAM_STACK_K = [102, 143, 163, 256, 311, 334, 360, 428, 512]
+DREAM_STACK_K = [102, 143, 163, 256, 311, 334, 360, 372, 428, 512]
 BATCHED_EXACT_RHO = [0.08, 0.16]                   # k = 327, 655 at N = 4096
 BATCHED_ID_RANKS = [64, 512]
 LLADA_ID_RANKS = [64, 256, 512]                    # the LLaDA stack's other proxy ranks
