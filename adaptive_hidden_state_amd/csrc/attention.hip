@@ -3,8 +3,9 @@
 //
 // One workgroup = one (sequence, query head, block of 32 QG queries). Its waves form QG query groups
 // (32 queries each) x KR key ranges: the keys are split into KR contiguous ranges, each streamed in
-// tiles of 32 keys through a double-buffered LDS stage that the QG waves of the range load together
-// and all read, so every K/V byte fetched from L2 serves 32 QG queries. QG = 2 halves the L2 traffic
+// tiles of 32 keys through LDS (QG = 1: one stage private to the range's wave; QG = 2: a
+// double-buffered stage that the two waves of the range load together and both read), so every K/V
+// byte fetched from L2 serves 32 QG queries. QG = 2 halves the L2 traffic
 // of QG = 1 but halves the number of workgroups; the launcher takes QG = 2 unless that would leave CUs
 // idle while QG = 1 fills them in one round. Each wave runs an online softmax over its range; the KR
 // partial results (running max, running sum, unnormalised output) of a query group are merged through
@@ -77,7 +78,8 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
   constexpr int KROWB = C::KROWB, VROWB = C::VROWB;
   constexpr int VEC = C::VEC;
   constexpr int KCH = KT * HD / VEC / (64 * kAttnQG);     // K 16-byte chunks per lane per tile
-  // V: bf16 uses 8x8 blocks (8 key rows x one 16-byte chunk); fp32 uses 4x4 blocks
+  // fp32 V goes in as 4-key x 4-dim blocks (transposed on the way into LDS); bf16 V rows take the K
+  // chunk mapping, and the block constants below are unused for it
   constexpr int VB = BF ? 8 : 4;
   constexpr int VTASKS = (KT / VB) * (HD / VB);           // blocks per tile
   constexpr int VW = (VTASKS + kAttnQG - 1) / kAttnQG;    // blocks per wave of a key range
@@ -121,8 +123,8 @@ __global__ __launch_bounds__((64 * AttnCfg<T, HD, QG>::W)) void attention_kernel
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
 
-  // Key range kr covers tiles [kr * tper, (kr + 1) * tper); every wave runs tper tiles (a barrier per
-  // tile), tiles past the end are clamped loads whose keys are all masked.
+  // Key range kr covers tiles [kr * tper, (kr + 1) * tper); every wave runs tper tiles (with a barrier
+  // per tile when the stage is shared), tiles past the end are clamped loads whose keys are all masked.
   const int ntiles = (n_tok + KT - 1) / KT;
   const int tper = (ntiles + KR - 1) / KR;
   const int t_begin = kr * tper;
