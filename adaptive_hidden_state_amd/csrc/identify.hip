@@ -15,9 +15,8 @@ namespace spa {
 // the cached proxy, write the new proxy. One wave per row, streaming the row in chunks of 64 lanes x 4
 // columns (16-byte accesses; r % 16 == 0), so any rank works, up to the full Value width. Each lane
 // reads its columns of the cached proxy before it writes the same columns, so the cache may be
-// updated in place (pc_write == pc_read).
-// One token per wave: its proxy row (split partials summed in order), the cosine against P^c, the
-// P^c / P writes and its 1 / rms.
+// updated in place (pc_write == pc_read). The same wave also writes the row's 1 / rms from the
+// per-split sums of squares (splits <= 64: one per lane).
 template <bool COHERENT = false>
 __device__ __forceinline__ void cosine_row(const float *__restrict__ part, int splits, int rows, int r, int row,
                                            const float *pc_read, float *pc_write, float *__restrict__ p_out,
