@@ -507,13 +507,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T *__restrict__ A, int 
 // 1..2 of the row so that both the copy (four lanes per row) and the MFMA fragment reads (32 rows
 // of one chunk) are free of bank conflicts; the packed weight blocks are copied as they are. Each
 // of the four waves owns a 128 x 128 quarter of the tile (16 accumulator blocks, 256 registers).
+// A 192-row variant (96 x 128 per wave) serves row counts just above a multiple of 256, where whole
+// 256-row tiles would compute up to a third of their rows for nothing.
 // ---------------------------------------------------------------------------------------------
-struct BigLds {
-  static constexpr int kStage = 32 * 1024;                // A 16 KB + B 16 KB of one 32-k slab
+template <int BM> struct BigLds {
+  static_assert(BM == 256 || BM == 192, "big tile rows");
+  static constexpr int kA = BM * 64;                      // A bytes of one 32-k slab
+  static constexpr int kStage = kA + 16 * 1024;           // + B 16 KB
   static constexpr int kStages = 4;
   static constexpr int kStride = 132;                     // staged output row (floats)
-  static constexpr int kEpi = 4 * 64 * kStride * 4;       // each wave's 64 x 128 half tile
+  static constexpr int kEpi = 4 * 64 * kStride * 4;       // each wave's 64 x 128 output rows at a time
   static constexpr int kBytes = kEpi > kStages * kStage ? kEpi : kStages * kStage;
+  static constexpr int CA = BM / 64;                      // A copy instructions per wave per slab
+  static constexpr int FM = BM / 64;                      // 32-row accumulator blocks per wave
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -551,11 +557,29 @@ __device__ __forceinline__ void lds_frags(const char *a, const char *b, u32x4 (&
       : "v"(va), "v"(vb), "i"(S * 1024), "i"((2 + S) * 1024), "i"((4 + S) * 1024), "i"((6 + S) * 1024)
       : "memory");
 }
+// The same with three A fragments (the 192-row tile): seven reads.
+template <int S>
+__device__ __forceinline__ void lds_frags(const char *a, const char *b, u32x4 (&af)[3], u32x4 (&bf)[4]) {
+  const uint32_t va = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)a;
+  const uint32_t vb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)b;
+  asm volatile(
+      "ds_read_b128 %0, %7\n\t"
+      "ds_read_b128 %1, %7 offset:2048\n\t"
+      "ds_read_b128 %2, %7 offset:4096\n\t"
+      "ds_read_b128 %3, %8 offset:%9\n\t"
+      "ds_read_b128 %4, %8 offset:%10\n\t"
+      "ds_read_b128 %5, %8 offset:%11\n\t"
+      "ds_read_b128 %6, %8 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
+      : "v"(va), "v"(vb), "i"(S * 1024), "i"((2 + S) * 1024), "i"((4 + S) * 1024), "i"((6 + S) * 1024)
+      : "memory");
+}
 
-// Per-thread copy plan of one slab: 4 A instructions (16 rows x 64 bytes each) and 4 weight-block
+// Per-thread copy plan of one slab: BM / 64 A instructions (16 rows x 64 bytes each) and 4 weight-block
 // instructions (1 KB each) per wave.
-struct BigCopy {
-  const char *a_src[4];  // this lane's source 16 bytes of each A instruction, at slab 0
+template <int BM> struct BigCopy {
+  const char *a_src[BM / 64];  // this lane's source 16 bytes of each A instruction, at slab 0
   const char *b_src[2];  // this lane's 16 bytes of the wave's two weight column blocks, at slab 0
   int wave;
   int nk;
@@ -565,23 +589,25 @@ struct BigCopy {
 // tell the fragment reads of one stage from the copies in flight into the others and needs no wait
 // for them; the copies a stage's reads depend on are waited for explicitly (each wave its own,
 // then a barrier).
+template <int BM>
 __device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__restrict__ s1, char *__restrict__ s2,
-                                              char *__restrict__ s3, const BigCopy &cp, int wm, int wn, int lane,
-                                              floatx16 (&acc)[4][4]) {
+                                              char *__restrict__ s3, const BigCopy<BM> &cp, int wm, int wn, int lane,
+                                              floatx16 (&acc)[BM / 64][4]) {
+  constexpr int CA = BigLds<BM>::CA, FM = BigLds<BM>::FM, KA = BigLds<BM>::kA;
   const int nk = cp.nk;
-  // fragment offsets: A row wm 128 + 32 i + lane % 32, logical chunk 2 s + lane / 32 (swizzled);
+  // fragment offsets: A row wm BM / 2 + 32 i + lane % 32, logical chunk 2 s + lane / 32 (swizzled);
   // weight block (wn 4 + j, k-step s)
-  const int arow = wm * 128 + (lane & 31), sw = ((lane & 31) >> 1) & 3;
+  const int arow = wm * (BM / 2) + (lane & 31), sw = ((lane & 31) >> 1) & 3;
   const int a_off0 = arow * 64 + ((0 + (lane >> 5)) ^ sw) * 16;
   const int a_off1 = arow * 64 + ((2 + (lane >> 5)) ^ sw) * 16;
-  const int b_off = 16384 + (wn * 8) * 1024 + lane * 16;
-  const int dst_a = cp.wave * 4 * 1024, dst_b = 16384 + cp.wave * 4 * 1024;
+  const int b_off = KA + (wn * 8) * 1024 + lane * 16;
+  const int dst_a = cp.wave * CA * 1024, dst_b = KA + cp.wave * 4 * 1024;
 
 // Slab KT (clamped) into stage DST.
 #define SPA_BIG_ISSUE(KT, DST)                                                                         \
   do {                                                                                                 \
     const int kc_ = min((KT), nk - 1);                                                                 \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
+    _Pragma("unroll") for (int j = 0; j < CA; ++j)                                                     \
         copy_to_lds(cp.a_src[j] + (size_t)kc_ * 64, (DST) + dst_a + j * 1024);                        \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
         copy_to_lds(cp.b_src[j >> 1] + ((size_t)kc_ * 2 + (j & 1)) * 1024, (DST) + dst_b + j * 1024);  \
@@ -591,16 +617,16 @@ __device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__res
 // reading before the barrier.
 #define SPA_BIG_STEP(KT, CUR, NXT)                                                                     \
   do {                                                                                                 \
-    wait_vmem<16>();                                                                                   \
+    wait_vmem<2 * (CA + 4)>();                                                                         \
     __builtin_amdgcn_s_barrier();                                                                      \
     SPA_BIG_ISSUE((KT) + 3, NXT);                                                                      \
     {                                                                                                  \
-      u32x4 af[4], bf[4];                                                                              \
+      u32x4 af[FM], bf[4];                                                                             \
       lds_frags<0>((CUR) + a_off0, (CUR) + b_off, af, bf);                                             \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
           _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
       lds_frags<1>((CUR) + a_off1, (CUR) + b_off, af, bf);                                             \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
           _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
     }                                                                                                  \
   } while (0)
@@ -619,15 +645,16 @@ __device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__res
   wait_vmem<0>();  // no copy may land in LDS after this point
 }
 
-template <int KIND>
+template <int KIND, int BM>
 __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict__ A, int lda,
                                                        const char *__restrict__ W, int wkb, int M, int N, int K,
                                                        int tiles_m, int tiles_n, EpiArgs ea) {
   typedef bf16_t T;
-  constexpr int BM = 256, BN = 256;
-  constexpr int STAGE = BigLds::kStage, ES = BigLds::kStride;
+  typedef BigLds<BM> L;
+  constexpr int BN = 256;
+  constexpr int STAGE = L::kStage, ES = L::kStride, CA = L::CA, FM = L::FM;
   constexpr bool NORM = KIND == kEpiQKV || KIND == kEpiSwiGLU;
-  __shared__ __attribute__((aligned(1024))) char lds[BigLds::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[L::kBytes];
   __shared__ float row_scale[NORM ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -646,16 +673,16 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict_
   const int tm = first_m + in_g % gsize;
   const int tn = in_g / gsize;
 
-  // copy plan: A instruction j of a wave covers rows r0 .. r0 + 15 (r0 = 16 (4 wave + j)); lane l
+  // copy plan: A instruction j of a wave covers rows r0 .. r0 + 15 (r0 = 16 (CA wave + j)); lane l
   // lands at LDS byte 16 l of it, i.e. row r0 + l / 4, physical chunk l % 4, and so fetches logical
   // chunk (l % 4) ^ ((row >> 1) & 3) of that row. Weight instruction j copies block 4 wave + j of the
   // slab (column block 2 wave + j / 2, k-step j % 2).
-  BigCopy cp;
+  BigCopy<BM> cp;
   cp.wave = wave;
   cp.nk = K / 32;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 16 + (lane >> 2);
+  for (int j = 0; j < CA; ++j) {
+    const int row = (wave * CA + j) * 16 + (lane >> 2);
     const int m = min(tm * BM + row, M - 1);
     size_t gr = (size_t)m;
     if (NORM && ea.idx != nullptr) {  // A rows gathered through the update set
@@ -674,6 +701,9 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict_
   }
 
   auto norm_scales = [&]() {
+    if constexpr (BM < 256) {
+      if (tid >= BM) return;  // one thread per row
+    }
     if (ea.row_rinv != nullptr) {
       const int m = min(tm * BM + tid, M - 1);
       size_t src = (size_t)m;
@@ -694,32 +724,36 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const bf16_t *__restrict_
     }
   };
 
-  floatx16 acc[4][4];
+  floatx16 acc[FM][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
   if constexpr (NORM) norm_scales();  // visible after the loop's barriers (and the one below)
-  if (cp.nk > 0) big_main_loop(lds, lds + STAGE, lds + 2 * STAGE, lds + 3 * STAGE, cp, wm, wn, lane, acc);
+  if (cp.nk > 0) big_main_loop<BM>(lds, lds + STAGE, lds + 2 * STAGE, lds + 3 * STAGE, cp, wm, wn, lane, acc);
   __syncthreads();
 
-  // Epilogue in two halves of 64 rows per wave: stage row-major in the wave's own LDS region (the
-  // wave reads back only what it wrote), then every lane finishes eight consecutive columns of a row.
-  constexpr int ER = 64, EC = 128;
-  float *ep = reinterpret_cast<float *>(lds) + wave * ER * ES;
+  // Epilogue in passes of up to 64 rows per wave (two; the 192-row tile's second pass has 32): stage
+  // row-major in the wave's own LDS region (the wave reads back only what it wrote), then every lane
+  // finishes eight consecutive columns of a row.
+  constexpr int EC = 128;
+  float *ep = reinterpret_cast<float *>(lds) + wave * 64 * ES;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    const int ER = h == 0 ? 64 : BM / 2 - 64;  // rows of this pass
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int ii = 0; ii < 2; ++ii) {
+      if (2 * h + ii >= FM) break;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q)
           ep[(ii * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3)) * ES + j * 32 + (lane & 31)] = acc[2 * h + ii][j][q];
-    const int rbase = wm * 128 + h * 64;  // row of the tile
+    }
+    const int rbase = wm * (BM / 2) + h * 64;  // row of the tile
     const int mbase = tm * BM + rbase, nbase = tn * BN + wn * EC;
     if constexpr (KIND == kEpiSwiGLU) {
       for (int idx = lane; idx < ER * EC / 16; idx += 64) {
@@ -1303,11 +1337,13 @@ GemmPlan plan_small(int dtype, int M, int N, int K, int kind, double *cost_out) 
   return best;
 }
 
-// The 256 x 256 kernel (bf16, no split): one 32-k slab per ~70 clocks when its tiles fit in one round,
-// ~75 under full load (measured over M = 256 .. 8192, N = 3584 .. 37888).
-double big_cost(int M, int N, int K) {
-  const long long tiles = (long long)ceil_div(M, 256) * ceil_div(N, 256);
-  return (double)ceil_div_ll(tiles, kCUs) * K * (tiles <= kCUs ? 70.0 : 75.0);
+// The large-M kernel (bf16, no split), 256 x 256 tiles: one 32-k slab per ~70 clocks when its tiles
+// fit in one round, ~75 under full load (measured over M = 256 .. 8192, N = 3584 .. 37888); 192 x 256
+// tiles take 0.82 of that per round (measured on the Dream gate/up, N = 37888, K = 3584: ~100 us for
+// a round of 256 tiles against ~120).
+double big_cost(int bm, int M, int N, int K) {
+  const long long tiles = (long long)ceil_div(M, bm) * ceil_div(N, 256);
+  return (double)ceil_div_ll(tiles, kCUs) * K * (tiles <= kCUs ? 70.0 : 75.0) * (bm == 256 ? 1.0 : 0.82);
 }
 }  // namespace
 
@@ -1329,36 +1365,41 @@ GemmPlan plan_gemm(int dtype, int M, int N, int K, int kind) {
   double cost;
   GemmPlan best = plan_small(dtype, M, N, K, kind, &cost);
   if (dtype != kBF16 || kind == kEpiPartial) return best;
-  GemmPlan big{};
-  big.cfg = kBigTileCfg;
-  big.bm = big.bn = 256;
-  big.splits = 1;
-  big.k_split = K;
-  big.tiles_m = ceil_div(M, 256);
-  big.tiles_n = ceil_div(N, 256);
-  // the 256 x 256 kernel wins once its tiles fill the chip
-  const double c_big = big_cost(M, N, K);
-  if (c_big < cost) {
-    best = big;
-    cost = c_big;
-  }
-  // SwiGLU at up to 512 rows with a last round of 256 x 256 tiles less than half full: the columns of
-  // the whole rounds on the 256 x 256 kernel, the rest on the best smaller tile (measured on the Dream
-  // gate/up at M = 512: 142 + 31 us against 210 for the best single launch, at M = 428 132 + 31
-  // against 189; at M = 2616 on the llada gate/up it measured level to 1.5% slower, so larger M keep
-  // one launch)
-  const long long tiles = (long long)big.tiles_m * big.tiles_n;
-  if (kind == kEpiSwiGLU && big.tiles_m <= 2 && tiles > kCUs && tiles % kCUs < kCUs / 2) {
-    const int tn0 = (int)((tiles / kCUs) * kCUs / big.tiles_m);  // tile columns of the whole rounds
-    if (tn0 > 0 && tn0 < big.tiles_n) {
-      const int n0 = tn0 * 256;
-      double c_tail;
-      plan_small(dtype, M, N - n0, K, kind, &c_tail);
-      const double c_split = big_cost(M, n0, K) + c_tail;
-      if (c_split < cost) {
-        best = big;
-        best.tiles_n = tn0;
-        best.n_main = n0;
+  for (const int bm : {256, 192}) {
+    GemmPlan big{};
+    big.cfg = bm == 256 ? kBigTileCfg : kBig192Cfg;
+    big.bm = bm;
+    big.bn = 256;
+    big.splits = 1;
+    big.k_split = K;
+    big.tiles_m = ceil_div(M, bm);
+    big.tiles_n = ceil_div(N, 256);
+    // the large-M kernel wins once its tiles fill the chip
+    const double c_big = big_cost(bm, M, N, K);
+    if (c_big < cost) {
+      best = big;
+      cost = c_big;
+    }
+    // SwiGLU at up to two row tiles with a last round of tiles less than half full: the columns of the
+    // whole rounds on the large-M kernel, the rest on the best smaller tile (measured on the Dream
+    // gate/up at M = 512: 142 + 31 us against 210 for the best single launch, at M = 428 132 + 31
+    // against 189; at M = 334 .. 384 192 x 256 rounds and the tail took 122-125 us against 151-155
+    // for 256 x 256 rounds and the tail; at M = 2616 on the llada gate/up it measured level to 1.5%
+    // slower, so larger M keep one launch)
+    const long long tiles = (long long)big.tiles_m * big.tiles_n;
+    if (kind == kEpiSwiGLU && big.tiles_m <= 2 && tiles > kCUs && tiles % kCUs < kCUs / 2) {
+      const int tn0 = (int)((tiles / kCUs) * kCUs / big.tiles_m);  // tile columns of the whole rounds
+      if (tn0 > 0 && tn0 < big.tiles_n) {
+        const int n0 = tn0 * 256;
+        double c_tail;
+        plan_small(dtype, M, N - n0, K, kind, &c_tail);
+        const double c_split = big_cost(bm, M, n0, K) + c_tail;
+        if (c_split < cost) {
+          best = big;
+          best.tiles_n = tn0;
+          best.n_main = n0;
+          cost = c_split;
+        }
       }
     }
   }
@@ -1422,9 +1463,14 @@ static hipError_t run_cfg(const GemmPlan &p, const void *A, int lda, const void 
       case 3: return run_gemm<T, 128, 64, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
       case 4: return run_gemm<T, 64, 128, KIND>(p, A, lda, W, wkb, M, N, K, part, ea, s);
       case kBigTileCfg:
+      case kBig192Cfg:
         if constexpr (KIND != kEpiPartial) {
-          hipLaunchKernelGGL(gemm_big_kernel<KIND>, dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256), 0, s,
-                             (const bf16_t *)A, lda, (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, ea);
+          if (p.cfg == kBigTileCfg)
+            hipLaunchKernelGGL((gemm_big_kernel<KIND, 256>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256), 0, s,
+                               (const bf16_t *)A, lda, (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, ea);
+          else
+            hipLaunchKernelGGL((gemm_big_kernel<KIND, 192>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(256), 0, s,
+                               (const bf16_t *)A, lda, (const char *)W, wkb, M, N, K, p.tiles_m, p.tiles_n, ea);
           return hipGetLastError();
         }
         return hipErrorInvalidValue;
@@ -1465,9 +1511,9 @@ static hipError_t run_kind(int kind, const GemmPlan &p, const void *A, int lda, 
 hipError_t launch_gemm(int dtype, int kind, const GemmPlan &plan, const void *A, int lda, const void *W, int wkb,
                        int M, int N, int K, float *part, const EpiArgs &ea, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (plan.n_main > 0) {  // SwiGLU: whole rounds of 256 x 256 tiles, then the remaining columns
+  if (plan.n_main > 0) {  // SwiGLU: whole rounds of large-M tiles, then the remaining columns
     const int n0 = plan.n_main;
-    if (dtype != kBF16 || kind != kEpiSwiGLU || plan.cfg != kBigTileCfg || n0 % 256 != 0 || n0 >= N ||
+    if (dtype != kBF16 || kind != kEpiSwiGLU || (plan.cfg != kBigTileCfg && plan.cfg != kBig192Cfg) || n0 % 256 != 0 || n0 >= N ||
         plan.tiles_n != n0 / 256)
       return hipErrorInvalidValue;
     GemmPlan pm = plan;

@@ -70,8 +70,10 @@ struct GemmPlan {
   int n_main;
 };
 
-// Tile configuration of the large-M kernel: bf16 only, 256 x 256 tiles, never split, no kEpiPartial.
+// Tile configurations of the large-M kernel: bf16 only, 256 x 256 (or 192 x 256) tiles, never split,
+// no kEpiPartial.
 constexpr int kBigTileCfg = 6;
+constexpr int kBig192Cfg = 17;
 // Tile configurations of the LDS-DMA small-M kernel (bf16, no kEpiPartial): kDmaCfg0 + i for tiles
 // kDmaTiles[i] (BM x BN).
 constexpr int kDmaCfg0 = 7;

@@ -3,9 +3,9 @@
 //
 // With no argument: over a sweep of shapes, every GEMM plan must cover the output with its tiles and K
 // with its splits, keep split-K within the partial workspace bound, and pick only kernels valid for
-// the shape (the LDS-DMA and 256 x 256 kernels: bf16, no partial-only output; split-K never for the
+// the shape (the LDS-DMA and large-M kernels: bf16, no partial-only output; split-K never for the
 // SwiGLU or QKV epilogues, whose RMSNorm needs all of K; a column split only for SwiGLU on whole
-// rounds of 256 x 256 tiles).
+// rounds of large-M tiles, 256 x 256 or 192 x 256).
 //
 // With "instances": reads lines "tag dtype B N d hq hkv hd F r k mode" from stdin (mode step: the
 // cached step with Top-k of k rows; full: the full recompute; identify: spa_identify; sparse:
@@ -49,7 +49,8 @@ static int sweep() {
             const GemmPlan p = plan_gemm(dtype, M, N, K, kind);
             ++plans;
             if (p.n_main != 0) ++splits_n;
-            const bool big = p.cfg == kBigTileCfg, dma = p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount;
+            const bool big = p.cfg == kBigTileCfg || p.cfg == kBig192Cfg;
+            const bool dma = p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount;
             const bool proxy = p.cfg == kProxyCfg;
             int bm = 0, bn = 0;
             if (proxy) {
@@ -58,7 +59,8 @@ static int sweep() {
               if (dtype != kBF16 || kind != kEpiPartial || N != 128)
                 fail("proxy kernel outside the bf16 rank-128 projection", dtype, M, N, K, kind, p);
             } else if (big) {
-              bm = bn = 256;
+              bm = p.cfg == kBigTileCfg ? 256 : 192;
+              bn = 256;
             } else if (dma) {
               bm = kDmaTiles[p.cfg - kDmaCfg0][0];
               bn = kDmaTiles[p.cfg - kDmaCfg0][1];
@@ -70,7 +72,7 @@ static int sweep() {
               continue;
             }
             if (p.bm != bm || p.bn != bn) fail("tile size does not match the configuration", dtype, M, N, K, kind, p);
-            if (p.n_main != 0) {  // SwiGLU: whole rounds of 256 x 256 tiles over n_main columns, then the rest
+            if (p.n_main != 0) {  // SwiGLU: whole rounds of large-M tiles over n_main columns, then the rest
               if (kind != kEpiSwiGLU || dtype != kBF16 || !big || p.n_main % 256 != 0 || p.n_main <= 0 ||
                   p.n_main >= N || p.tiles_n != p.n_main / 256 ||
                   (long long)p.tiles_m * p.tiles_n > (long long)p.tiles_m * ((N + 255) / 256) / 256 * 256)
@@ -84,8 +86,8 @@ static int sweep() {
               fail("splits do not cover K exactly once", dtype, M, N, K, kind, p);
             if (dtype == kF32 && p.cfg != 5) fail("fp32 takes the 64 x 64 register tile only", dtype, M, N, K, kind, p);
             if ((big || dma) && (dtype != kBF16 || kind == kEpiPartial))
-              fail("LDS-DMA / 256-tile kernel outside bf16 products", dtype, M, N, K, kind, p);
-            if (big && p.splits != 1) fail("the 256 x 256 kernel never splits K", dtype, M, N, K, kind, p);
+              fail("LDS-DMA / large-M kernel outside bf16 products", dtype, M, N, K, kind, p);
+            if (big && p.splits != 1) fail("the large-M kernel never splits K", dtype, M, N, K, kind, p);
             if (p.splits > 1) {
               if (kind == kEpiSwiGLU || kind == kEpiQKV) fail("split-K of a normalised epilogue", dtype, M, N, K, kind, p);
               if ((long long)p.tiles_m * p.tiles_n * p.splits > kMaxSplitWGs)
@@ -106,8 +108,8 @@ static std::string tile_name(int dtype, const GemmPlan &p) {
   char b[64];
   if (p.cfg == kProxyCfg)
     snprintf(b, sizeof b, "proxy%dx%d", p.bm, p.bn);
-  else if (p.cfg == kBigTileCfg)
-    snprintf(b, sizeof b, "big256x256");
+  else if (p.cfg == kBigTileCfg || p.cfg == kBig192Cfg)
+    snprintf(b, sizeof b, "big%dx256", p.bm);
   else if (p.cfg >= kDmaCfg0 && p.cfg < kDmaCfg0 + kDmaTileCount)
     snprintf(b, sizeof b, "dma%dx%d", p.bm, p.bn);
   else
