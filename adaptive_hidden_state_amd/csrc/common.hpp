@@ -124,6 +124,17 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += xor_lane<1>(v);
   return v;
 }
+// The same butterfly over each aligned group of G lanes (G = 16, 32 or 64; G = 64 is wave_sum).
+template <int G> __device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 16 || G == 32 || G == 64, "group size");
+  if constexpr (G == 64) v += xor_lane<32>(v);
+  if constexpr (G >= 32) v += xor_lane<16>(v);
+  v += xor_lane<8>(v);
+  v += xor_lane<4>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<1>(v);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, xor_lane<32>(v));
   v = fmaxf(v, xor_lane<16>(v));

@@ -9,24 +9,28 @@
 namespace spa {
 
 // ---------------------------------------------------------------------------------------------
-// partial-sum reduce + cosine + proxy-cache write; one wave per token row
+// partial-sum reduce + cosine + proxy-cache write; 16, 32 or 64 lanes per token row
 // ---------------------------------------------------------------------------------------------
 // Reduce the proxy GEMM's split-K partials (in split order: deterministic), take the cosine against
-// the cached proxy, write the new proxy. One wave per row, streaming the row in chunks of 64 lanes x 4
-// columns (16-byte accesses; r % 16 == 0), so any rank works, up to the full Value width. Each lane
-// reads its columns of the cached proxy before it writes the same columns, so the cache may be
-// updated in place (pc_write == pc_read). The same wave also writes the row's 1 / rms from the
-// per-split sums of squares (splits <= 64: one per lane).
-template <bool COHERENT = false>
-__device__ __forceinline__ void cosine_row(const float *__restrict__ part, int splits, int rows, int r, int row,
+// the cached proxy, write the new proxy. LPR lanes serve one row (64 / LPR rows per wave), streaming it
+// in chunks of LPR lanes x 4 columns (16-byte accesses; r % 16 == 0), so any rank works, up to the full
+// Value width; ranks up to 128 take 32 lanes per row and up to 64 take 16, so no lane idles on a short
+// row. Each lane reads its columns of the cached proxy before it writes the same columns, so the cache
+// may be updated in place (pc_write == pc_read). The same lanes also write the row's 1 / rms from the
+// per-split sums of squares. Every lane of the wave calls this (the sums cross lanes); `ok` is false for
+// a row past the end, whose loads are clamped to the last row and whose stores are skipped.
+template <bool COHERENT = false, int LPR = 64>
+__device__ __forceinline__ void cosine_row(const float *__restrict__ part, int splits, int rows, int r, int row, bool ok,
                                            const float *pc_read, float *pc_write, float *__restrict__ p_out,
                                            float *scores, const float *__restrict__ ss_part, int d, float eps,
                                            float *__restrict__ rinv) {
-  const int lane = threadIdx.x & 63;
+  static_assert(LPR == 16 || LPR == 32 || LPR == 64, "lanes per row");
+  const int sl = threadIdx.x & (LPR - 1);  // lane within the row's group
   const size_t plane = (size_t)rows * r;
+  if (!ok) row = rows - 1;
   const size_t base = (size_t)row * r;
   float dot = 0.f, n1 = 0.f, n2 = 0.f;
-  for (int col = lane * 4; col < r; col += 256) {
+  for (int col = sl * 4; col < r; col += 4 * LPR) {
     floatx4 v = *reinterpret_cast<const floatx4 *>(part + base + col);
     // the other splits eight at a time: the loads of a group are all in flight before the first add
     // (one memory round trip per group instead of one per split; measured 1 us off the fused kernel
@@ -51,21 +55,23 @@ __device__ __forceinline__ void cosine_row(const float *__restrict__ part, int s
         n2 += w[x] * w[x];
       }
     }
-    if (p_out != nullptr) *reinterpret_cast<floatx4 *>(p_out + base + col) = v;
-    if (pc_write != nullptr) *reinterpret_cast<floatx4 *>(pc_write + base + col) = v;
+    if (ok && p_out != nullptr) *reinterpret_cast<floatx4 *>(p_out + base + col) = v;
+    if (ok && pc_write != nullptr) *reinterpret_cast<floatx4 *>(pc_write + base + col) = v;
   }
-  // the row's 1 / rms for the RMSNorm fused into the QKV GEMM (split partials summed in order)
-  if (rinv != nullptr) {  // lane sp holds split sp's partial; a fixed reduction tree adds them
-    float ss = lane < splits ? ss_part[(size_t)lane * rows + row] : 0.f;
-    ss = wave_sum(ss);
-    if (lane == 0) rinv[row] = 1.0f / sqrtf(ss / (float)d + eps);
+  // the row's 1 / rms for the RMSNorm fused into the QKV GEMM: lane sl adds splits sl, sl + LPR, ... in
+  // that order, then a fixed reduction tree over the row's lanes
+  if (rinv != nullptr) {
+    float ss = 0.f;
+    for (int sp = sl; sp < splits; sp += LPR) ss += ss_part[(size_t)sp * rows + row];
+    ss = group_sum<LPR>(ss);
+    if (ok && sl == 0) rinv[row] = 1.0f / sqrtf(ss / (float)d + eps);
   }
   if (pc_read != nullptr && scores != nullptr) {
-    dot = wave_sum(dot);
-    n1 = wave_sum(n1);
-    n2 = wave_sum(n2);
+    dot = group_sum<LPR>(dot);
+    n1 = group_sum<LPR>(n1);
+    n2 = group_sum<LPR>(n2);
     const float c = dot / (fmaxf(sqrtf(n1), 1e-8f) * fmaxf(sqrtf(n2), 1e-8f));
-    if (lane == 0) {
+    if (ok && sl == 0) {
       if constexpr (COHERENT)
         __hip_atomic_store(scores + row, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else
@@ -74,22 +80,37 @@ __device__ __forceinline__ void cosine_row(const float *__restrict__ part, int s
   }
 }
 
+// Lanes per row of the cosine pass for proxy rank r (each lane takes 4 columns per chunk).
+int cosine_lanes_per_row(int r) { return r <= 64 ? 16 : (r <= 128 ? 32 : 64); }
+
+template <int LPR>
 __global__ __launch_bounds__(256) void proxy_cosine_kernel(const float *__restrict__ part, int splits, int rows,
                                                            int r, const float *pc_read, float *pc_write,
                                                            float *__restrict__ p_out, float *__restrict__ scores,
                                                            const float *__restrict__ ss_part, int d, float eps,
                                                            float *__restrict__ rinv) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  cosine_row(part, splits, rows, r, row, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv);
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + (threadIdx.x & 63) / LPR;
+  if ((blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW >= rows) return;  // whole waves past the end
+  cosine_row<false, LPR>(part, splits, rows, r, row, row < rows, pc_read, pc_write, p_out, scores, ss_part, d, eps,
+                         rinv);
 }
 
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read, float *pc_write,
                                float *p_out, float *scores, const float *ss_part, int d, float eps, float *rinv,
                                hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(proxy_cosine_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, part, splits, rows, r, pc_read,
-                     pc_write, p_out, scores, ss_part, d, eps, rinv);
+  const int lpr = cosine_lanes_per_row(r), per_wg = 4 * (64 / lpr);
+  const dim3 grid((rows + per_wg - 1) / per_wg), block(256);
+  if (lpr == 16)
+    hipLaunchKernelGGL(proxy_cosine_kernel<16>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv);
+  else if (lpr == 32)
+    hipLaunchKernelGGL(proxy_cosine_kernel<32>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv);
+  else
+    hipLaunchKernelGGL(proxy_cosine_kernel<64>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out,
+                       scores, ss_part, d, eps, rinv);
   return hipGetLastError();
 }
 
@@ -298,35 +319,32 @@ __device__ void topk_block(const float *s, int n, int k, int32_t *out, TopkShare
   }
 
   // Emit in index order: keys whose resolved bits are below the prefix, plus those equal to it --
-  // all of them when the last bin fitted exactly, else the first `krem` in index order.
+  // all of them when the last bin fitted exactly, else the first `krem` in index order. Thread t holds
+  // the contiguous index range [start, start + chunk), so a key's output position is the number of
+  // keys below the prefix at lower indices plus the number of boundary keys taken at lower indices,
+  // min(equal keys before it, krem). One exclusive scan yields both counts: below-prefix keys in the
+  // low 16 bits, equal keys in the high 16 (n <= 16384, so neither field carries into the other).
   const uint32_t mask = hi >= 31 ? 0u : (0xffffffffu << (hi + 1));
-  uint32_t r = 0;
-  if (!full) {
-    uint32_t ceq = 0;
+  const uint32_t eq_cap = full ? 0xffffffffu : krem;
+  uint32_t cnt = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) ceq += (((valid >> j) & 1ull) && (key[j] & mask) == prefix) ? 1u : 0u;
-    r = block_exclusive_scan(ceq, wsum);
+  for (int j = 0; j < PER; ++j) {
+    if (!((valid >> j) & 1ull)) continue;
+    const uint32_t km = key[j] & mask;
+    cnt += km < prefix ? 1u : (km == prefix ? 0x10000u : 0u);
   }
-  uint64_t sel = 0;
-  uint32_t csel = 0;
+  // no closing barrier: callers pass a barrier before the shared state is written again
+  const uint32_t before = block_exclusive_scan_open(cnt, wsum);
+  uint32_t eq = before >> 16;
+  uint32_t pos = (before & 0xffffu) + min(eq, eq_cap);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     if (!((valid >> j) & 1ull)) continue;
     const uint32_t km = key[j] & mask;
     bool take = km < prefix;
-    if (km == prefix) {
-      take = full || r < krem;
-      ++r;
-    }
-    if (take) {
-      sel |= 1ull << j;
-      ++csel;
-    }
+    if (km == prefix) take = eq++ < eq_cap;
+    if (take && pos < (uint32_t)k) out[pos++] = start + j;
   }
-  uint32_t pos = block_exclusive_scan(csel, wsum);
-#pragma unroll
-  for (int j = 0; j < PER; ++j)
-    if (((sel >> j) & 1ull) && pos < (uint32_t)k) out[pos++] = start + j;
 }
 
 template <int PER>
@@ -338,16 +356,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
 }
 
 // The cosine pass fused with the Top-k of each sequence (n tokens per sequence, k of them selected):
-// every workgroup scores eight tokens as proxy_cosine_kernel, then adds the number of its tokens in each
-// sequence to that sequence's counter; the workgroup whose addition completes a sequence runs the
-// Top-k of that sequence (topk_block with all kTopkThreads = 512 threads) and resets its counter to
+// every workgroup scores 8 (64 / LPR) tokens as proxy_cosine_kernel, then adds the number of its tokens
+// in each sequence to that sequence's counter; the workgroup whose addition completes a sequence runs
+// the Top-k of that sequence (topk_block with all kTopkThreads = 512 threads) and resets its counter to
 // 0. The scores cross workgroups through agent-scope atomic stores and loads, which are coherent
-// across the XCDs' L2 caches without cache-wide write-backs or invalidations (release / acquire fences would flush the
-// whole L2, including this kernel's P^c writes); each wave waits until its score store has completed
-// before the workgroup's counter addition, which is itself an agent-scope atomic, and the Top-k's
-// loads are issued only after that addition returned the completing count. The counters must be 0 at
-// launch (the proxy projection that precedes this kernel clears them).
-template <int PER>
+// across the XCDs' L2 caches without cache-wide write-backs or invalidations (release / acquire fences
+// would flush the whole L2, including this kernel's P^c writes); each wave waits until its score stores
+// have completed before the workgroup's counter addition, which is itself an agent-scope atomic, and the
+// Top-k's loads are issued only after that addition returned the completing count. Rows of two lanes
+// groups per wave (LPR = 32) halve the workgroups, and with them the additions to one counter, against
+// a wave per row. The counters must be 0 at launch (the proxy projection that precedes this kernel
+// clears them).
+template <int PER, int LPR>
 __global__ __launch_bounds__(kTopkThreads) void cosine_topk_kernel(const float *__restrict__ part, int splits,
                                                                    int rows, int r, const float *pc_read,
                                                                    float *pc_write, float *__restrict__ p_out,
@@ -355,13 +375,17 @@ __global__ __launch_bounds__(kTopkThreads) void cosine_topk_kernel(const float *
                                                                    int d, float eps, float *__restrict__ rinv, int n,
                                                                    int k, int32_t *__restrict__ idx_out,
                                                                    uint32_t *counters) {
-  constexpr int RW = kTopkThreads / 64;  // rows (one per wave) of a workgroup
+  constexpr int RPW = 64 / LPR;                      // rows per wave
+  constexpr int RW = kTopkThreads / 64 * RPW;        // rows of a workgroup
   __shared__ TopkShared sh;
   __shared__ uint32_t last[RW];
   const int tid = threadIdx.x, row0 = blockIdx.x * RW;
-  const int row = row0 + (tid >> 6);
-  if (row < rows) cosine_row<true>(part, splits, rows, r, row, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's memory operations (its score store included) completed
+  const int wrow0 = row0 + (tid >> 6) * RPW;         // first row of this wave
+  const int row = wrow0 + (tid & 63) / LPR;
+  if (wrow0 < rows)  // uniform over the wave
+    cosine_row<true, LPR>(part, splits, rows, r, row, row < rows, pc_read, pc_write, p_out, scores, ss_part, d, eps,
+                          rinv);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's memory operations (its score stores included) completed
   __syncthreads();
   if (tid == 0) {  // the (at most RW) sequences of this workgroup's rows, in order
     int nl = 0;
@@ -386,17 +410,16 @@ __global__ __launch_bounds__(kTopkThreads) void cosine_topk_kernel(const float *
   }
 }
 
-hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, int r, const float *pc_read,
-                              float *pc_write, float *p_out, float *scores, const float *ss_part, int d, float eps,
-                              float *rinv, int k, int32_t *idx_out, uint32_t *counters, hipStream_t s) {
-  const int rows = batch * n;
-  if (rows <= 0) return hipSuccess;
-  if (n > 32 * kTopkThreads || k <= 0 || pc_read == nullptr || scores == nullptr) return hipErrorInvalidValue;
-  constexpr int RW = kTopkThreads / 64;
+template <int LPR>
+hipError_t launch_cosine_topk_lpr(const float *part, int splits, int rows, int n, int r, const float *pc_read,
+                                  float *pc_write, float *p_out, float *scores, const float *ss_part, int d,
+                                  float eps, float *rinv, int k, int32_t *idx_out, uint32_t *counters,
+                                  hipStream_t s) {
+  constexpr int RW = kTopkThreads / 64 * (64 / LPR);
   const dim3 grid((rows + RW - 1) / RW), block(kTopkThreads);
-#define SPA_COSINE_TOPK(PER)                                                                                     \
-  hipLaunchKernelGGL(cosine_topk_kernel<PER>, grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, p_out, \
-                     scores, ss_part, d, eps, rinv, n, k, idx_out, counters)
+#define SPA_COSINE_TOPK(PER)                                                                                       \
+  hipLaunchKernelGGL((cosine_topk_kernel<PER, LPR>), grid, block, 0, s, part, splits, rows, r, pc_read, pc_write, \
+                     p_out, scores, ss_part, d, eps, rinv, n, k, idx_out, counters)
   if (n <= 2 * kTopkThreads)
     SPA_COSINE_TOPK(2);
   else if (n <= 4 * kTopkThreads)
@@ -409,6 +432,23 @@ hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, i
     SPA_COSINE_TOPK(32);
 #undef SPA_COSINE_TOPK
   return hipGetLastError();
+}
+
+hipError_t launch_cosine_topk(const float *part, int splits, int batch, int n, int r, const float *pc_read,
+                              float *pc_write, float *p_out, float *scores, const float *ss_part, int d, float eps,
+                              float *rinv, int k, int32_t *idx_out, uint32_t *counters, hipStream_t s) {
+  const int rows = batch * n;
+  if (rows <= 0) return hipSuccess;
+  if (n > 32 * kTopkThreads || k <= 0 || pc_read == nullptr || scores == nullptr) return hipErrorInvalidValue;
+  const int lpr = cosine_lanes_per_row(r);
+  if (lpr == 16)
+    return launch_cosine_topk_lpr<16>(part, splits, rows, n, r, pc_read, pc_write, p_out, scores, ss_part, d, eps,
+                                      rinv, k, idx_out, counters, s);
+  if (lpr == 32)
+    return launch_cosine_topk_lpr<32>(part, splits, rows, n, r, pc_read, pc_write, p_out, scores, ss_part, d, eps,
+                                      rinv, k, idx_out, counters, s);
+  return launch_cosine_topk_lpr<64>(part, splits, rows, n, r, pc_read, pc_write, p_out, scores, ss_part, d, eps, rinv,
+                                    k, idx_out, counters, s);
 }
 
 int topk_keys_per_thread(int n, bool fused) {

@@ -128,6 +128,8 @@ hipError_t launch_pack_weight(int dtype, int kind, int rows, int cols, const voi
 constexpr int kFusedTopkRows = 8192;
 // Keys held per thread by the Top-k of an n-token sequence (fused: inside the cosine kernel).
 int topk_keys_per_thread(int n, bool fused);
+// Lanes that serve one hidden row in the cosine pass at proxy rank r (16, 32 or 64).
+int cosine_lanes_per_row(int r);
 // ss_part (splits x rows, nullable): the proxy GEMM's per-split sums of squares of each hidden row;
 // with rinv set, rinv[row] = 1 / sqrt(sum / d + eps) is written as well.
 hipError_t launch_proxy_cosine(const float *part, int splits, int rows, int r, const float *pc_read,

@@ -52,6 +52,8 @@ DREAM_STACK_K = [102, 143, 163, 256, 311, 334, 360, 372, 428, 512]
 BATCHED_EXACT_RHO = [0.08, 0.16]                   # k = 327, 655 at N = 4096
 BATCHED_ID_RANKS = [64, 512]
 LLADA_ID_RANKS = [64, 256, 512]                    # the LLaDA stack's other proxy ranks
+# cached steps at another proxy rank (the stacks' rank sweep): (workload, rank, exactly k drifted rows)
+RANK_STEP_CASES = [("llada", 256, 51), ("dream", 256, 102)]
 
 LLADA = synth.WORKLOADS["llada-layer"].shape
 DREAM = synth.WORKLOADS["dream-stack"].shape
@@ -98,6 +100,7 @@ def parity_calls():
     calls += [(BATCHED, int(BATCHED.n_tokens * rho + 1e-9), "step") for rho in BATCHED_EXACT_RHO]
     calls += [(BATCHED.replace(rank=r), 0, "identify") for r in BATCHED_ID_RANKS]
     calls += [(LLADA.replace(rank=r), 0, "identify") for r in LLADA_ID_RANKS]
+    calls += [({"llada": LLADA, "dream": DREAM}[wl].replace(rank=r), k, "step") for wl, r, k in RANK_STEP_CASES]
     for dtype, hd, hq, hkv, n, m in ATTEND_CASES:
         calls.append((synth.LayerShape(2, n, 256, hq, hkv, hd, 256, 16, dtype), m, "attend"))
     for b, hd, hq, hkv, n, m in ATTEND_MANY_CASES:

@@ -181,10 +181,11 @@ static int instances() {
       const int rows = s.B * s.N;
       printf(" %s", gemm_key("proxy", s.dtype, rows, s.r, s.d, kEpiPartial, P.proxy).c_str());
       const char *wide = s.r > 256 ? ":wide" : "";
+      const int lpr = cosine_lanes_per_row(s.r);
       if (P.identify == kIdFusedTopk)
-        printf(" cos+topk:per%d%s", topk_keys_per_thread(s.N, true), wide);
+        printf(" cos+topk:per%d:lpr%d%s", topk_keys_per_thread(s.N, true), lpr, wide);
       else
-        printf(" cos%s", wide);
+        printf(" cos:lpr%d%s", lpr, wide);
       if (P.identify == kIdSeparateTopk) printf(" topk:per%d", topk_keys_per_thread(s.N, false));
     } else {
       printf(" rinv");

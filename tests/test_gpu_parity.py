@@ -13,8 +13,8 @@ import oracle
 import synth
 from helpers import check_near_ties, dev, has_gpu, host, rel_l2, tol_for
 from parity_cases import (ATTEND_CASES, ATTEND_MANY_CASES, BATCHED_EXACT_RHO, BATCHED_ID_RANKS, DREAM_STACK_K,
-                          FUSED_TOPK_SHAPES, LLADA_EXACT_K, LLADA_ID_RANKS, ROPE_STEP_CASES, SMALL_BF16, SMALL_STEP_K,
-                          fused_topk_ks)
+                          FUSED_TOPK_SHAPES, LLADA_EXACT_K, LLADA_ID_RANKS, RANK_STEP_CASES, ROPE_STEP_CASES,
+                          SMALL_BF16, SMALL_STEP_K, fused_topk_ks)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs an MI355X")]
 
@@ -615,6 +615,30 @@ def test_dream_layer_step_full_value_identifier(dream_case):
     c.cache0 = oracle.LayerCache(c.cache0.k, c.cache0.v, c.cache0.h,
                                  oracle.proxy(c.x0, c.w_r).astype(np.float32).astype(np.float64))
     _check_step(c, 102, exact=True)
+
+
+def _with_proxy(case, w_r):
+    """The same case with another singular proxy W_r (its rank from W_r's rows): the cached proxies of
+    the warm-up input recomputed under it."""
+    case.w_r = w_r
+    case.shape = case.shape.replace(rank=w_r.shape[0])
+    case.cache0 = oracle.LayerCache(case.cache0.k, case.cache0.v, case.cache0.h,
+                                    oracle.proxy(case.x0, w_r).astype(np.float32).astype(np.float64))
+    return case
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("wl,r,k", RANK_STEP_CASES)
+def test_layer_step_other_rank_full_size(llada_case, dream_case, wl, r, k):
+    """Cached steps of the llada and Dream layers at proxy rank r (the stacks' rank sweep: the cosine
+    pass then serves a row per wave, against two rows per wave at rank 128), exactly k drifted rows."""
+    base = llada_case if wl == "llada" else dream_case
+    c = _redrift(base, k, 7)
+    if wl == "llada":
+        w_r = base.w_rs[r]
+    else:
+        w_r = synth.to_storage(oracle.singular_proxy(c.w["w_v"], c.w["g_attn"], r), c.shape.dtype)
+    _check_step(_with_proxy(c, w_r), k, exact=True)
 
 
 @pytest.mark.timeout(900)
