@@ -145,6 +145,9 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// A compile-time flag passed to generic lambdas (bodies instantiated with and without a step).
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 

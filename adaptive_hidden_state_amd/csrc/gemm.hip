@@ -1192,7 +1192,12 @@ __global__ __launch_bounds__(256) void proxy_gemm_kernel(const bf16_t *__restric
   __syncthreads();
   const int nk_pad = (nk + PF - 1) / PF * PF;
   const int frag_off = (lane & 31) * ROWB + (lane >> 5) * 16;
-  for (int kt0 = 0; kt0 < nk_pad; kt0 += PF) {
+  // One group of PF slabs; LOAD: refill each slot with the slab PF ahead. The last group issues no
+  // loads (every slab it would fetch lies past the end), so no clamped re-read of the last slab is
+  // requested (at 8 slabs per workgroup, PF = 4, that was a third of the loads), and its waits stay
+  // exact in straight-line code.
+  auto group = [&](int kt0, auto load_tag) {
+    constexpr bool LOAD = decltype(load_tag)::value;
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int kt = kt0 + u;
@@ -1202,10 +1207,12 @@ __global__ __launch_bounds__(256) void proxy_gemm_kernel(const bf16_t *__restric
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma32(ld16(As + s * 32), rb[u][s], acc);
       }
-      gload(kt + PF, ra[u], rb[u]);
+      if constexpr (LOAD) gload(kt + PF, ra[u], rb[u]);
       __syncthreads();
     }
-  }
+  };
+  for (int kt0 = 0; kt0 + PF < nk_pad; kt0 += PF) group(kt0, BoolTag<true>{});
+  if (nk_pad > 0) group(nk_pad - PF, BoolTag<false>{});
 
   // lane holds column 32 wave + lane % 32 and rows 8 (q / 4) + 4 (lane / 32) + q % 4 of the tile
   float *pp = part + (size_t)split * M * kProxyCols + wave * 32 + (lane & 31);
