@@ -363,10 +363,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
 // across the XCDs' L2 caches without cache-wide write-backs or invalidations (release / acquire fences
 // would flush the whole L2, including this kernel's P^c writes); each wave waits until its score stores
 // have completed before the workgroup's counter addition, which is itself an agent-scope atomic, and the
-// Top-k's loads are issued only after that addition returned the completing count. Rows of two lanes
-// groups per wave (LPR = 32) halve the workgroups, and with them the additions to one counter, against
-// a wave per row. The counters must be 0 at launch (the proxy projection that precedes this kernel
-// clears them).
+// Top-k's loads are issued only after that addition returned the completing count. Two rows per wave
+// (LPR = 32) give half the workgroups of one row per wave, and so half the additions to each counter.
+// The counters must be 0 at launch (the proxy projection that precedes this kernel clears them).
 template <int PER, int LPR>
 __global__ __launch_bounds__(kTopkThreads) void cosine_topk_kernel(const float *__restrict__ part, int splits,
                                                                    int rows, int r, const float *pc_read,
