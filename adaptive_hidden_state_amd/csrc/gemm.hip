@@ -535,46 +535,19 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Eight 16-byte LDS reads (four at a + 2048 i, four at b + 1024 (2 j + S)) in one block that also
-// waits for them, so the results are complete when the block ends. The compiler does not see these
-// reads as LDS accesses and so adds no wait for copies in flight into other stages; the caller
-// orders them after the stage's copies (explicit wait and barrier).
-template <int S>
-__device__ __forceinline__ void lds_frags(const char *a, const char *b, u32x4 (&af)[4], u32x4 (&bf)[4]) {
-  const uint32_t va = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)a;
-  const uint32_t vb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)b;
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:2048\n\t"
-      "ds_read_b128 %2, %8 offset:4096\n\t"
-      "ds_read_b128 %3, %8 offset:6144\n\t"
-      "ds_read_b128 %4, %9 offset:%10\n\t"
-      "ds_read_b128 %5, %9 offset:%11\n\t"
-      "ds_read_b128 %6, %9 offset:%12\n\t"
-      "ds_read_b128 %7, %9 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
-      : "v"(va), "v"(vb), "i"(S * 1024), "i"((2 + S) * 1024), "i"((4 + S) * 1024), "i"((6 + S) * 1024)
-      : "memory");
+// The same copy issued from inline asm (M0 = the wave-uniform LDS base, one wait state between the M0
+// write and the copy that reads it): the compiler does not see it as an LDS write, so it puts no wait
+// for copies in flight before later LDS reads, which it can then schedule among the MFMAs; the caller
+// orders those reads after the copies they depend on (explicit vmcnt wait and barrier). The copy
+// writes no register, so the compiler may reuse its address registers once it has issued.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is a reserved register; the clobber says it changes
+__device__ __forceinline__ void copy_to_lds_asm(const void *g, const char *l) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)l);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
 }
-// The same with three A fragments (the 192-row tile): seven reads.
-template <int S>
-__device__ __forceinline__ void lds_frags(const char *a, const char *b, u32x4 (&af)[3], u32x4 (&bf)[4]) {
-  const uint32_t va = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)a;
-  const uint32_t vb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)b;
-  asm volatile(
-      "ds_read_b128 %0, %7\n\t"
-      "ds_read_b128 %1, %7 offset:2048\n\t"
-      "ds_read_b128 %2, %7 offset:4096\n\t"
-      "ds_read_b128 %3, %8 offset:%9\n\t"
-      "ds_read_b128 %4, %8 offset:%10\n\t"
-      "ds_read_b128 %5, %8 offset:%11\n\t"
-      "ds_read_b128 %6, %8 offset:%12\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3])
-      : "v"(va), "v"(vb), "i"(S * 1024), "i"((2 + S) * 1024), "i"((4 + S) * 1024), "i"((6 + S) * 1024)
-      : "memory");
-}
+#pragma clang diagnostic pop
 
 // Per-thread copy plan of one slab: BM / 64 A instructions (16 rows x 64 bytes each) and 4 weight-block
 // instructions (1 KB each) per wave.
@@ -608,9 +581,9 @@ __device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__res
   do {                                                                                                 \
     const int kc_ = min((KT), nk - 1);                                                                 \
     _Pragma("unroll") for (int j = 0; j < CA; ++j)                                                     \
-        copy_to_lds(cp.a_src[j] + (size_t)kc_ * 64, (DST) + dst_a + j * 1024);                        \
+        copy_to_lds_asm(cp.a_src[j] + (size_t)kc_ * 64, (DST) + dst_a + j * 1024);                    \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                      \
-        copy_to_lds(cp.b_src[j >> 1] + ((size_t)kc_ * 2 + (j & 1)) * 1024, (DST) + dst_b + j * 1024);  \
+        copy_to_lds_asm(cp.b_src[j >> 1] + ((size_t)kc_ * 2 + (j & 1)) * 1024, (DST) + dst_b + j * 1024); \
   } while (0)
 // Slab KT from stage CUR after this wave's copies of it landed (slabs KT + 1, KT + 2 may stay in
 // flight) and every wave passed the barrier; slab KT + 3 into stage NXT, which every wave finished
@@ -620,12 +593,11 @@ __device__ __forceinline__ void big_main_loop(char *__restrict__ s0, char *__res
     wait_vmem<2 * (CA + 4)>();                                                                         \
     __builtin_amdgcn_s_barrier();                                                                      \
     SPA_BIG_ISSUE((KT) + 3, NXT);                                                                      \
-    {                                                                                                  \
+    _Pragma("unroll") for (int h_ = 0; h_ < 2; ++h_) {                                                 \
       u32x4 af[FM], bf[4];                                                                             \
-      lds_frags<0>((CUR) + a_off0, (CUR) + b_off, af, bf);                                             \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
-          _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
-      lds_frags<1>((CUR) + a_off1, (CUR) + b_off, af, bf);                                             \
+      const char *ar_ = (CUR) + (h_ ? a_off1 : a_off0), *br_ = (CUR) + b_off + h_ * 1024;              \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] = ld16(ar_ + i * 2048);                     \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) bf[j] = ld16(br_ + j * 2048);                      \
       _Pragma("unroll") for (int i = 0; i < FM; ++i)                                                   \
           _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);   \
     }                                                                                                  \
