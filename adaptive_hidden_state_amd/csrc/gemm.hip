@@ -535,19 +535,27 @@ template <int N> __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// The same copy issued from inline asm (M0 = the wave-uniform LDS base, one wait state between the M0
-// write and the copy that reads it): the compiler does not see it as an LDS write, so it puts no wait
-// for copies in flight before later LDS reads, which it can then schedule among the MFMAs; the caller
-// orders those reads after the copies they depend on (explicit vmcnt wait and barrier). The copy
-// writes no register, so the compiler may reuse its address registers once it has issued.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is a reserved register; the clobber says it changes
+// The same copy issued from inline asm: the compiler does not see it as an LDS write, so it puts no
+// wait for copies in flight before later LDS reads, which it can then schedule among the MFMAs; the
+// caller orders those reads after the copies they depend on (explicit vmcnt wait and barrier). M0
+// takes the wave-uniform LDS base for the copy (one wait state between the M0 write and the copy
+// that reads it) and gets its previous value back afterwards, so no value the compiler keeps in M0
+// is lost. The copy writes no register, so its address registers may be reused once it has issued.
 __device__ __forceinline__ void copy_to_lds_asm(const void *g, const char *l) {
   const uint32_t m0 =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)l);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(g)
+      : "memory");
 }
-#pragma clang diagnostic pop
 
 // Per-thread copy plan of one slab: BM / 64 A instructions (16 rows x 64 bytes each) and 4 weight-block
 // instructions (1 KB each) per wave.
